@@ -1,0 +1,18 @@
+"""fp64 CPU oracle for headwise-chunked causal GQA attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this package: only the tests, the smoke check of __graft_entry__ and the
+cpu_baseline leg of bench.py use it.  It shares no code with the HIP library.
+"""
+from .attention import (  # noqa: F401
+    attention_bwd_head,
+    attention_fwd_head,
+    attention_rows,
+    dq_rows,
+    kv_grad_tail,
+    layer_bwd,
+    layer_fwd,
+    layer_rows,
+    rope,
+    rope_angles,
+)
