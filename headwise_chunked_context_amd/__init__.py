@@ -1,0 +1,22 @@
+"""Headwise-chunked causal GQA attention (UPipe) for MI355X / gfx950.
+
+The layer runs in the HIP library libupipe_attn.so (C ABI in
+include/upipe_attn.h); this package is its thin ctypes binding.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS,
+    PASS_BWD,
+    PASS_FWD,
+    UPIPE_ECHUNK,
+    UPIPE_EHIP,
+    UPIPE_EINVAL,
+    UPIPE_EUNSUPPORTED,
+    UPIPE_EWORKSPACE,
+    UPIPE_OK,
+    UpipeError,
+    attn_bwd,
+    attn_fwd,
+    lib,
+    strerror,
+    workspace_bytes,
+)

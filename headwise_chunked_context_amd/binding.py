@@ -1,0 +1,153 @@
+"""ctypes binding of libupipe_attn.so (argument marshalling only).
+
+Every step of the layer runs in the HIP library; this module only turns torch
+tensors into device pointers, allocates outputs and the workspace with torch,
+and raises on a non-zero status.  If the library is missing it fails loudly:
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libupipe_attn.so")
+
+UPIPE_OK = 0
+UPIPE_EINVAL = -1
+UPIPE_EUNSUPPORTED = -2
+UPIPE_ECHUNK = -3
+UPIPE_EWORKSPACE = -4
+UPIPE_EHIP = -5
+PASS_FWD = 0
+PASS_BWD = 1
+
+# names declared in include/upipe_attn.h
+EXPORTS = (
+    "upipe_attn_workspace_bytes",
+    "upipe_attn_fwd",
+    "upipe_attn_bwd",
+    "upipe_strerror",
+    "upipe_version",
+)
+
+
+class UpipeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {strerror(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m headwise_chunked_context_amd.build`"
+        )
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, f64, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
+    vp = ctypes.c_void_p
+    L.upipe_attn_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.upipe_attn_workspace_bytes.restype = ctypes.c_int
+    L.upipe_attn_fwd.argtypes = [i64, i32, i32, i32, i32, f64, i32,
+                                 vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.upipe_attn_fwd.restype = ctypes.c_int
+    L.upipe_attn_bwd.argtypes = [i64, i32, i32, i32, i32, f64, i32,
+                                 vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.upipe_attn_bwd.restype = ctypes.c_int
+    L.upipe_strerror.argtypes = [ctypes.c_int]
+    L.upipe_strerror.restype = ctypes.c_char_p
+    L.upipe_version.argtypes = []
+    L.upipe_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().upipe_strerror(int(status)).decode()
+
+
+def workspace_bytes(L: int, hidden: int, n_q: int, n_kv: int, head_dim: int, head_chunk: int,
+                    pass_: int) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().upipe_attn_workspace_bytes(L, hidden, n_q, n_kv, head_dim, head_chunk, pass_,
+                                          ctypes.byref(out))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_attn_workspace_bytes")
+    return out.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes: int, device, workspace):
+    import torch
+
+    if workspace is not None:
+        return workspace
+    # 256-byte aligned by the caching allocator
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def attn_fwd(x, w_qkv, w_o, n_q: int, n_kv: int, head_chunk: int, theta: float,
+             head_dim: int = 128, workspace=None, stream=None):
+    """Forward of the chunked layer.  Returns (y or None, o_saved, lse).
+
+    x: bf16 [L, hidden] (projection mode) or packed q|k|v [L, (Hq+2Hkv)d]
+    when w_qkv is None.
+    """
+    import torch
+
+    L = x.shape[0]
+    proj = w_qkv is not None
+    hidden = x.shape[1] if proj else 0
+    dev = x.device
+    y = torch.empty(L, hidden, dtype=torch.bfloat16, device=dev) if proj else None
+    o_saved = torch.empty(L, n_q * head_dim, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(n_q, L, dtype=torch.float32, device=dev)
+    ws_n = workspace_bytes(L, hidden, n_q, n_kv, head_dim, head_chunk, PASS_FWD)
+    ws = _workspace(ws_n, dev, workspace)
+    rc = lib().upipe_attn_fwd(L, hidden, n_q, n_kv, head_dim, float(theta), head_chunk,
+                              _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(y), _ptr(o_saved), _ptr(lse),
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_attn_fwd")
+    return y, o_saved, lse
+
+
+def attn_bwd(x, w_qkv, w_o, o_saved, lse, dy, n_q: int, n_kv: int, head_chunk: int,
+             theta: float, head_dim: int = 128, workspace=None, stream=None):
+    """Backward of the chunked layer.  Returns (dx, dw_qkv, dw_o); in q/k/v-given
+    mode dx is dqkv and the weight gradients are None."""
+    import torch
+
+    L = x.shape[0]
+    proj = w_qkv is not None
+    hidden = x.shape[1] if proj else 0
+    dev = x.device
+    dx = torch.empty_like(x)
+    dw_qkv = torch.empty_like(w_qkv) if proj else None
+    dw_o = torch.empty_like(w_o) if proj else None
+    ws_n = workspace_bytes(L, hidden, n_q, n_kv, head_dim, head_chunk, PASS_BWD)
+    ws = _workspace(ws_n, dev, workspace)
+    rc = lib().upipe_attn_bwd(L, hidden, n_q, n_kv, head_dim, float(theta), head_chunk,
+                              _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(o_saved), _ptr(lse), _ptr(dy),
+                              _ptr(dx), _ptr(dw_qkv), _ptr(dw_o),
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_attn_bwd")
+    return dx, dw_qkv, dw_o

@@ -1,0 +1,534 @@
+// C ABI of the headwise-chunked causal GQA attention layer: argument checks,
+// workspace planning and the chunk scheduler (host side, one HIP stream).
+//
+// The schedule is the method's: one head chunk at a time, the chunk's rows of
+// W_qkv project its q (and k/v when a KV group is first touched), attention
+// runs, the per-head output is stored and the chunk's share of W_o
+// accumulates into y; the next chunk reuses the same workspace buffers
+// ("Untied Ulysses Pushes Llama-3-8B Training to 5 Million Tokens", Untied
+// Ulysses section).  A KV group stays resident in the workspace while any of
+// its query heads is being processed (grouped-query tailoring, same section).
+#include <math.h>
+#include <string.h>
+
+#include "../../include/upipe_attn.h"
+#include "kernels.h"
+
+using namespace upipe;
+
+namespace {
+
+constexpr int64_t kMaxL = int64_t(1) << 24;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up64(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+struct Shape {
+  int64_t L, Lp;
+  int D, Hq, Hkv, d, hc, G, kc;  // kc = KV heads a chunk touches
+  bool proj;
+};
+
+int check_shape(int64_t L, int32_t hidden, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                int32_t hc, Shape* s) {
+  if (L < 1 || hidden < 0 || n_q < 1 || n_kv < 1 || head_dim < 1 || hc < 1) return UPIPE_EINVAL;
+  if (n_q % n_kv != 0) return UPIPE_EINVAL;
+  if (head_dim != 128) return UPIPE_EUNSUPPORTED;
+  if (hidden % 128 != 0) return UPIPE_EUNSUPPORTED;
+  if (L > kMaxL) return UPIPE_EUNSUPPORTED;
+  const int G = n_q / n_kv;
+  if (n_q % hc != 0) return UPIPE_ECHUNK;
+  if (!(hc % G == 0 || G % hc == 0)) return UPIPE_ECHUNK;
+  s->L = L;
+  s->Lp = round_up64(L, 256);
+  s->D = hidden;
+  s->Hq = n_q;
+  s->Hkv = n_kv;
+  s->d = head_dim;
+  s->hc = hc;
+  s->G = G;
+  s->kc = hc >= G ? hc / G : 1;
+  s->proj = hidden > 0;
+  return UPIPE_OK;
+}
+
+// Split-K factor of the weight-gradient GEMMs (reduction over L): enough
+// workgroups to cover the 256 CUs twice, each split at least 256 rows.
+int dw_splits(int64_t L, int M, int N) {
+  int tiles = (M / 128) * (N / 128);
+  int s = (512 + tiles - 1) / tiles;
+  int max_by_len = (int)((L + 255) / 256);
+  if (s > max_by_len) s = max_by_len;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  return s;
+}
+int k_per_split(int64_t L, int splits) {
+  int64_t k = (L + splits - 1) / splits;
+  return (int)round_up64(k, 64);
+}
+
+// Workspace layout.  Every buffer that grows with the sequence is either
+// per q head of ONE chunk (hc) or per KV head a chunk touches (kc): the size
+// is affine in hc and independent of Hq.
+struct Plan {
+  size_t staging;              // [L][(hc+2kc)d] bf16 GEMM output / gradient staging
+  size_t q_rm, q_t;            // [hc][Lp][d] bf16 (q_t bwd only)
+  size_t k_rm, k_t, v_rm, v_t; // [kc][Lp][d] / [kc][d][Lp] bf16
+  size_t do_rm, do_t;          // [hc][Lp][d] bf16 (bwd)
+  size_t lse2, dvec;           // [hc][Lp] fp32 (bwd)
+  size_t dq_acc;               // [hc][Lp][d] fp32 (bwd)
+  size_t dk_acc, dv_acc;       // [kc][Lp][d] fp32 (bwd, only when a group spans chunks)
+  size_t dw_acc;               // fp32 weight-gradient accumulator (bwd, projection mode)
+  size_t total;
+};
+
+Plan make_plan(const Shape& s, int pass) {
+  Plan p;
+  memset(&p, 0, sizeof(p));
+  const size_t Lp = (size_t)s.Lp, d = (size_t)s.d, hc = (size_t)s.hc, kc = (size_t)s.kc;
+  const size_t width = (hc + 2 * kc) * d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t head_bf16 = Lp * d * 2;
+  const size_t no = (size_t)-1;
+  p.staging = s.proj ? take((size_t)s.L * width * 2) : no;
+  p.q_rm = take(hc * head_bf16);
+  p.q_t = pass == UPIPE_PASS_BWD ? take(hc * head_bf16) : no;
+  p.k_rm = take(kc * head_bf16);
+  p.k_t = pass == UPIPE_PASS_BWD ? take(kc * head_bf16) : no;
+  p.v_rm = pass == UPIPE_PASS_BWD ? take(kc * head_bf16) : no;
+  p.v_t = pass == UPIPE_PASS_FWD ? take(kc * head_bf16) : no;
+  if (pass == UPIPE_PASS_BWD) {
+    p.do_rm = take(hc * head_bf16);
+    p.do_t = take(hc * head_bf16);
+    p.lse2 = take(hc * Lp * 4);
+    p.dvec = take(hc * Lp * 4);
+    p.dq_acc = take(hc * Lp * d * 4);
+    // cross-chunk dK/dV accumulators (used while a KV group spans chunks;
+    // always reserved so the size stays affine in the chunk)
+    p.dk_acc = take(kc * Lp * d * 4);
+    p.dv_acc = take(kc * Lp * d * 4);
+    // fp32 split-K accumulator of the weight gradients: dW_o[:, cols(c)] is
+    // [D][hc d], dW_qkv[rows(c)] is [(hc+2kc) d][D]
+    p.dw_acc = s.proj ? take(width * (size_t)s.D * 4) : no;
+  } else {
+    p.do_rm = p.do_t = p.lse2 = p.dvec = p.dq_acc = p.dk_acc = p.dv_acc = p.dw_acc = no;
+  }
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return off == (size_t)-1 ? nullptr : reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+RopeTable make_rope(double theta, int d) {
+  RopeTable t;
+  for (int i = 0; i < d / 2; ++i)
+    t.rev_per_pos[i] = pow(theta, -2.0 * i / d) / (2.0 * M_PI);
+  return t;
+}
+
+int check_common(const Shape& s, double theta, const void* x, const void* w_qkv, const void* w_o,
+                 void* ws, size_t ws_bytes, int pass) {
+  if (!(theta > 0.0) || !isfinite(theta)) return UPIPE_EINVAL;
+  if (!x) return UPIPE_EINVAL;
+  if (s.proj != (w_qkv != nullptr) || s.proj != (w_o != nullptr)) return UPIPE_EINVAL;
+  if (!aligned16(x) || (w_qkv && !aligned16(w_qkv)) || (w_o && !aligned16(w_o))) return UPIPE_EINVAL;
+  Plan p = make_plan(s, pass);
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0 || ws_bytes < p.total)
+    return UPIPE_EWORKSPACE;
+  return UPIPE_OK;
+}
+
+#define UPIPE_TRY(expr)                   \
+  do {                                    \
+    if ((expr) != hipSuccess) return UPIPE_EHIP; \
+  } while (0)
+
+struct Chunk {
+  int h0;        // first q head
+  int g0;        // first KV group touched
+  int nkv;       // KV groups touched (kc)
+  bool kv_first; // the chunk starts its KV groups (project / prepare K, V)
+  bool kv_last;  // the chunk finishes its KV groups
+};
+
+Chunk chunk_info(const Shape& s, int c) {
+  Chunk ch;
+  ch.h0 = c * s.hc;
+  ch.g0 = ch.h0 / s.G;
+  ch.nkv = s.kc;
+  ch.kv_first = (ch.h0 % s.G) == 0;
+  ch.kv_last = ((ch.h0 + s.hc) % s.G) == 0;
+  return ch;
+}
+
+// Stage the chunk's q (and k, v when it starts a group) in GEMM output
+// layout: staging[L][hc*d | kc*d | kc*d].
+int project_chunk(const Shape& s, const Chunk& ch, const uint16_t* x, const uint16_t* w_qkv,
+                  uint16_t* staging, hipStream_t st) {
+  const int d = s.d;
+  const int width = (s.hc + 2 * s.kc) * d;
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A = x;
+  g.lda = s.D;
+  g.B = w_qkv;
+  g.ldb = s.D;
+  g.bseg.count = ch.kv_first ? 3 : 1;
+  g.bseg.end[0] = s.hc * d;
+  g.bseg.row0[0] = (int64_t)ch.h0 * d;
+  g.bseg.end[1] = (s.hc + s.kc) * d;
+  g.bseg.row0[1] = (int64_t)(s.Hq + ch.g0) * d;
+  g.bseg.end[2] = width;
+  g.bseg.row0[2] = (int64_t)(s.Hq + s.Hkv + ch.g0) * d;
+  g.C = staging;
+  g.ldc = width;
+  g.M = (int)s.L;
+  g.N = ch.kv_first ? width : s.hc * d;
+  g.K = s.D;
+  g.k_per_split = s.D;
+  UPIPE_TRY(launch_gemm(GEMM_NT, EPI_STORE_BF16, g, st));
+  return UPIPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int upipe_version(void) { return 100; }
+
+const char* upipe_strerror(int status) {
+  switch (status) {
+    case UPIPE_OK: return "ok";
+    case UPIPE_EINVAL: return "invalid argument (sizes, head counts, pointers or theta)";
+    case UPIPE_EUNSUPPORTED: return "unsupported shape (head_dim must be 128, hidden a multiple of 128, L <= 2^24)";
+    case UPIPE_ECHUNK: return "head_chunk must divide n_q_heads and not split a KV group's query heads";
+    case UPIPE_EWORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than upipe_attn_workspace_bytes";
+    case UPIPE_EHIP: return "HIP runtime error while launching a kernel";
+    default: return "unknown status";
+  }
+}
+
+int upipe_attn_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, int32_t head_chunk,
+                               int32_t pass, size_t* bytes) {
+  if (!bytes || (pass != UPIPE_PASS_FWD && pass != UPIPE_PASS_BWD)) return UPIPE_EINVAL;
+  Shape s;
+  int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
+  if (rc != UPIPE_OK) return rc;
+  *bytes = make_plan(s, pass).total;
+  return UPIPE_OK;
+}
+
+int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
+                   int32_t head_dim, double rope_theta, int32_t head_chunk, const uint16_t* x,
+                   const uint16_t* w_qkv, const uint16_t* w_o, uint16_t* y, uint16_t* o_saved,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
+  if (rc != UPIPE_OK) return rc;
+  rc = check_common(s, rope_theta, x, w_qkv, w_o, workspace, workspace_bytes, UPIPE_PASS_FWD);
+  if (rc != UPIPE_OK) return rc;
+  if (!o_saved || !lse || s.proj != (y != nullptr)) return UPIPE_EINVAL;
+  if (!aligned16(o_saved) || !aligned16(lse) || (y && !aligned16(y))) return UPIPE_EINVAL;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Plan p = make_plan(s, UPIPE_PASS_FWD);
+  const RopeTable rope = make_rope(rope_theta, s.d);
+  const int d = s.d;
+  uint16_t* staging = at<uint16_t>(workspace, p.staging);
+  uint16_t* q_rm = at<uint16_t>(workspace, p.q_rm);
+  uint16_t* k_rm = at<uint16_t>(workspace, p.k_rm);
+  uint16_t* v_t = at<uint16_t>(workspace, p.v_t);
+  const int64_t qkv_ld = (int64_t)(s.Hq + 2 * s.Hkv) * d;
+  const int width = (s.hc + 2 * s.kc) * d;
+
+  for (int c = 0; c < s.Hq / s.hc; ++c) {
+    const Chunk ch = chunk_info(s, c);
+    // 1. chunked QKV projection (or pick the given q/k/v columns) + RoPE
+    PrepArgs pa;
+    memset(&pa, 0, sizeof(pa));
+    if (s.proj) {
+      rc = project_chunk(s, ch, x, w_qkv, staging, st);
+      if (rc != UPIPE_OK) return rc;
+      pa.src_q = staging;
+      pa.src_k = staging + s.hc * d;
+      pa.src_v = staging + (s.hc + s.kc) * d;
+      pa.src_ld = width;
+    } else {
+      pa.src_q = x + (int64_t)ch.h0 * d;
+      pa.src_k = x + (int64_t)(s.Hq + ch.g0) * d;
+      pa.src_v = x + (int64_t)(s.Hq + s.Hkv + ch.g0) * d;
+      pa.src_ld = qkv_ld;
+    }
+    pa.nq = s.hc;
+    pa.nkv = ch.kv_first ? s.kc : 0;
+    pa.q_rm = q_rm;
+    pa.k_rm = k_rm;
+    pa.v_t = v_t;
+    pa.L = s.L;
+    pa.Lp = s.Lp;
+    UPIPE_TRY(launch_prep_qkv(pa, rope, st));
+
+    // 2. causal attention of the chunk's heads; stores O and LSE
+    FwdArgs fa;
+    fa.q = q_rm;
+    fa.k = k_rm;
+    fa.vt = v_t;
+    fa.nh = s.hc;
+    fa.group = s.G;
+    fa.q_head0 = ch.h0;
+    fa.kv_head0 = ch.g0;
+    fa.o = o_saved;
+    fa.o_ld = (int64_t)s.Hq * d;
+    fa.lse = lse;
+    fa.L = s.L;
+    fa.Lp = s.Lp;
+    fa.scale_log2 = kLog2e / sqrtf((float)d);
+    UPIPE_TRY(launch_flash_fwd(fa, st));
+
+    // 3. y (+)= O_c W_o[:, cols(c)]^T
+    if (s.proj) {
+      GemmArgs g;
+      memset(&g, 0, sizeof(g));
+      g.A = o_saved + (int64_t)ch.h0 * d;
+      g.lda = (int64_t)s.Hq * d;
+      g.B = w_o + (int64_t)ch.h0 * d;
+      g.ldb = (int64_t)s.Hq * d;
+      g.C = y;
+      g.ldc = s.D;
+      g.M = (int)s.L;
+      g.N = s.D;
+      g.K = s.hc * d;
+      g.k_per_split = g.K;
+      UPIPE_TRY(launch_gemm(GEMM_NT, c == 0 ? EPI_STORE_BF16 : EPI_ACCUM_BF16, g, st));
+    }
+  }
+  return UPIPE_OK;
+}
+
+int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
+                   int32_t head_dim, double rope_theta, int32_t head_chunk, const uint16_t* x,
+                   const uint16_t* w_qkv, const uint16_t* w_o, const uint16_t* o_saved,
+                   const float* lse, const uint16_t* dy, uint16_t* dx, uint16_t* dw_qkv,
+                   uint16_t* dw_o, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
+  if (rc != UPIPE_OK) return rc;
+  rc = check_common(s, rope_theta, x, w_qkv, w_o, workspace, workspace_bytes, UPIPE_PASS_BWD);
+  if (rc != UPIPE_OK) return rc;
+  if (!o_saved || !lse || !dy || !dx) return UPIPE_EINVAL;
+  if (s.proj != (dw_qkv != nullptr) || s.proj != (dw_o != nullptr)) return UPIPE_EINVAL;
+  if (!aligned16(o_saved) || !aligned16(lse) || !aligned16(dy) || !aligned16(dx) ||
+      (dw_qkv && !aligned16(dw_qkv)) || (dw_o && !aligned16(dw_o)))
+    return UPIPE_EINVAL;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Plan p = make_plan(s, UPIPE_PASS_BWD);
+  const RopeTable rope = make_rope(rope_theta, s.d);
+  const int d = s.d;
+  const int64_t qkv_ld = (int64_t)(s.Hq + 2 * s.Hkv) * d;
+  const int width = (s.hc + 2 * s.kc) * d;
+  uint16_t* staging = at<uint16_t>(workspace, p.staging);
+  uint16_t* q_rm = at<uint16_t>(workspace, p.q_rm);
+  uint16_t* q_t = at<uint16_t>(workspace, p.q_t);
+  uint16_t* k_rm = at<uint16_t>(workspace, p.k_rm);
+  uint16_t* k_t = at<uint16_t>(workspace, p.k_t);
+  uint16_t* v_rm = at<uint16_t>(workspace, p.v_rm);
+  uint16_t* do_rm = at<uint16_t>(workspace, p.do_rm);
+  uint16_t* do_t = at<uint16_t>(workspace, p.do_t);
+  float* lse2 = at<float>(workspace, p.lse2);
+  float* dvec = at<float>(workspace, p.dvec);
+  float* dq_acc = at<float>(workspace, p.dq_acc);
+  float* dk_acc = at<float>(workspace, p.dk_acc);
+  float* dv_acc = at<float>(workspace, p.dv_acc);
+  float* dw_acc = at<float>(workspace, p.dw_acc);
+
+  // accumulators start at zero; each finalize pass clears what it consumed
+  UPIPE_TRY(launch_zero(dq_acc, (size_t)s.hc * s.Lp * d * 4, st));
+  if (dw_acc) UPIPE_TRY(launch_zero(dw_acc, (size_t)width * s.D * 4, st));
+
+  for (int c = 0; c < s.Hq / s.hc; ++c) {
+    const Chunk ch = chunk_info(s, c);
+    // 1. recompute the chunk's rotated q (and k, v at a group start)
+    PrepArgs pa;
+    memset(&pa, 0, sizeof(pa));
+    if (s.proj) {
+      rc = project_chunk(s, ch, x, w_qkv, staging, st);
+      if (rc != UPIPE_OK) return rc;
+      pa.src_q = staging;
+      pa.src_k = staging + s.hc * d;
+      pa.src_v = staging + (s.hc + s.kc) * d;
+      pa.src_ld = width;
+    } else {
+      pa.src_q = x + (int64_t)ch.h0 * d;
+      pa.src_k = x + (int64_t)(s.Hq + ch.g0) * d;
+      pa.src_v = x + (int64_t)(s.Hq + s.Hkv + ch.g0) * d;
+      pa.src_ld = qkv_ld;
+    }
+    pa.nq = s.hc;
+    pa.nkv = ch.kv_first ? s.kc : 0;
+    pa.q_rm = q_rm;
+    pa.q_t = q_t;
+    pa.k_rm = k_rm;
+    pa.k_t = k_t;
+    pa.v_rm = v_rm;
+    pa.L = s.L;
+    pa.Lp = s.Lp;
+    UPIPE_TRY(launch_prep_qkv(pa, rope, st));
+
+    // 2. dO of the chunk's heads (dy W_o[:, cols] or the given dO) and dW_o
+    PrepDoutArgs pd;
+    pd.o = o_saved + (int64_t)ch.h0 * d;
+    pd.o_ld = (int64_t)s.Hq * d;
+    pd.lse = lse + (int64_t)ch.h0 * s.L;
+    pd.nh = s.hc;
+    pd.do_rm = do_rm;
+    pd.do_t = do_t;
+    pd.lse2 = lse2;
+    pd.dvec = dvec;
+    pd.L = s.L;
+    pd.Lp = s.Lp;
+    if (s.proj) {
+      GemmArgs g;
+      memset(&g, 0, sizeof(g));
+      g.A = dy;
+      g.lda = s.D;
+      g.B = w_o + (int64_t)ch.h0 * d;
+      g.ldb = (int64_t)s.Hq * d;
+      g.C = staging;
+      g.ldc = s.hc * d;
+      g.M = (int)s.L;
+      g.N = s.hc * d;
+      g.K = s.D;
+      g.k_per_split = s.D;
+      UPIPE_TRY(launch_gemm(GEMM_NN, EPI_STORE_BF16, g, st));
+      pd.src_do = staging;
+      pd.do_ld = s.hc * d;
+
+      // dW_o[:, cols] = dy^T O_c   (reduction over the sequence, split-K)
+      const int splits = dw_splits(s.L, s.D, s.hc * d);
+      GemmArgs w;
+      memset(&w, 0, sizeof(w));
+      w.A = dy;
+      w.lda = s.D;
+      w.B = o_saved + (int64_t)ch.h0 * d;
+      w.ldb = (int64_t)s.Hq * d;
+      w.C = dw_acc;
+      w.M = s.D;
+      w.N = s.hc * d;
+      w.K = (int)s.L;
+      w.k_per_split = k_per_split(s.L, splits);
+      UPIPE_TRY(launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, st));
+      RowSegments ident;
+      memset(&ident, 0, sizeof(ident));
+      UPIPE_TRY(launch_acc_to_bf16(dw_acc, s.D, s.hc * d, dw_o + (int64_t)ch.h0 * d,
+                                   (int64_t)s.Hq * d, ident, st));
+    } else {
+      pd.src_do = dy + (int64_t)ch.h0 * d;
+      pd.do_ld = (int64_t)s.Hq * d;
+    }
+    UPIPE_TRY(launch_prep_dout(pd, st));
+
+    // 3. attention backward: dQ into the fp32 accumulator, dK/dV of the groups
+    BwdArgs ba;
+    ba.q = q_rm;
+    ba.qt = q_t;
+    ba.k = k_rm;
+    ba.kt = k_t;
+    ba.v = v_rm;
+    ba.dO = do_rm;
+    ba.dOt = do_t;
+    ba.lse2 = lse2;
+    ba.dvec = dvec;
+    ba.dq_acc = dq_acc;
+    ba.dk_acc = dk_acc;
+    ba.dv_acc = dv_acc;
+    ba.kv_first = ch.kv_first ? 1 : 0;
+    ba.kv_last = ch.kv_last ? 1 : 0;
+    uint16_t* grad_base;   // rows of [dq | dk | dv] for this chunk
+    int64_t grad_ld;
+    if (s.proj) {
+      grad_base = staging;
+      grad_ld = width;
+      ba.dk_out = staging + s.hc * d;
+      ba.dv_out = staging + (s.hc + s.kc) * d;
+    } else {
+      grad_base = dx + (int64_t)ch.h0 * d;
+      grad_ld = qkv_ld;
+      ba.dk_out = dx + (int64_t)(s.Hq + ch.g0) * d;
+      ba.dv_out = dx + (int64_t)(s.Hq + s.Hkv + ch.g0) * d;
+    }
+    ba.out_ld = s.proj ? width : qkv_ld;
+    ba.nh = s.hc;
+    ba.nkv = s.kc;
+    ba.group = s.G;
+    ba.q_head0 = ch.h0;
+    ba.kv_head0 = ch.g0;
+    ba.L = s.L;
+    ba.Lp = s.Lp;
+    ba.scale_log2 = kLog2e / sqrtf((float)d);
+    ba.scale = 1.f / sqrtf((float)d);
+    ba.rope = rope;
+    UPIPE_TRY(launch_flash_bwd(ba, st));
+    UPIPE_TRY(launch_dq_finalize(dq_acc, s.hc, s.L, s.Lp, ba.scale, grad_base, grad_ld, rope, st));
+
+    // 4. dx (+)= [dq | dk | dv] W_qkv[rows], dW_qkv[rows] = [dq | dk | dv]^T x
+    if (s.proj) {
+      const int ncols = ch.kv_last ? width : s.hc * d;
+      RowSegments seg;
+      memset(&seg, 0, sizeof(seg));
+      seg.count = ch.kv_last ? 3 : 1;
+      seg.end[0] = s.hc * d;
+      seg.row0[0] = (int64_t)ch.h0 * d;
+      seg.end[1] = (s.hc + s.kc) * d;
+      seg.row0[1] = (int64_t)(s.Hq + ch.g0) * d;
+      seg.end[2] = width;
+      seg.row0[2] = (int64_t)(s.Hq + s.Hkv + ch.g0) * d;
+
+      GemmArgs g;
+      memset(&g, 0, sizeof(g));
+      g.A = staging;
+      g.lda = width;
+      g.B = w_qkv;
+      g.ldb = s.D;
+      g.bseg = seg;
+      g.C = dx;
+      g.ldc = s.D;
+      g.M = (int)s.L;
+      g.N = s.D;
+      g.K = ncols;
+      g.k_per_split = ncols;
+      UPIPE_TRY(launch_gemm(GEMM_NN, c == 0 ? EPI_STORE_BF16 : EPI_ACCUM_BF16, g, st));
+
+      const int splits = dw_splits(s.L, ncols, s.D);
+      GemmArgs w;
+      memset(&w, 0, sizeof(w));
+      w.A = staging;
+      w.lda = width;
+      w.B = x;
+      w.ldb = s.D;
+      w.C = dw_acc;
+      w.M = ncols;
+      w.N = s.D;
+      w.K = (int)s.L;
+      w.k_per_split = k_per_split(s.L, splits);
+      UPIPE_TRY(launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, st));
+      UPIPE_TRY(launch_acc_to_bf16(dw_acc, ncols, s.D, dw_qkv, s.D, seg, st));
+    }
+  }
+  return UPIPE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,197 @@
+// Causal GQA flash-attention forward for one head chunk (gfx950, d = 128).
+//
+// Exact softmax attention evaluated tile by tile with a running maximum and
+// sum (FlashAttention, cited in the Builds-on list of "Untied Ulysses:
+// Memory-Efficient Context Parallelism via Headwise Chunking"); the chunk
+// loop that calls it is the headwise schedule of "Untied Ulysses Pushes
+// Llama-3-8B Training to 5 Million Tokens" (Untied Ulysses section).
+//
+// Layout choices for CDNA4:
+//  * a workgroup is 4 waves x 32 query rows = 128 queries of one q head;
+//    key/value tiles of 64 keys are staged in LDS (double-buffered, loads
+//    for tile t+1 issued before the MFMAs of tile t);
+//  * scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: each lane then owns ONE query and 16 keys of
+//    a 32-key block, so the row max/sum need one cross-half exchange
+//    (lane ^ 32) and the output rescale is a per-lane scalar;
+//  * the P^T accumulator registers feed the O^T = V^T P^T MFMA directly as
+//    its B operand (no LDS round trip); V^T comes from a d-major copy so the
+//    A operand reads are two 8-byte runs of keys;
+//  * the softmax runs in base 2 with the 1/sqrt(d) scale folded into one FMA;
+//  * workgroups are issued heaviest (last query tile) first, and consecutive
+//    workgroups take different heads of the chunk so the heads sharing a KV
+//    group spread over the XCDs while each XCD streams one head's K/V.
+#include "kernels.h"
+
+namespace upipe {
+namespace {
+
+constexpr int BM = 128;       // queries per workgroup
+constexpr int BN = 64;        // keys per step
+constexpr int KP = 128 + 8;   // K tile pitch (bf16)
+constexpr int VP = BN + 8;    // V^T tile pitch (bf16)
+
+__global__ __launch_bounds__(256) void flash_fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][128 * VP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+
+  const int nqt = (int)(a.Lp / BM);
+  const int head = blockIdx.x % a.nh;
+  const int qt = nqt - 1 - (int)(blockIdx.x / a.nh);
+  const int64_t q0 = (int64_t)qt * BM;
+  if (q0 >= a.L) return;  // whole tile is padding
+  const int kvh = (a.q_head0 + head) / a.group - a.kv_head0;
+  const uint16_t* qp = a.q + (int64_t)head * a.Lp * 128;
+  const uint16_t* kp = a.k + (int64_t)kvh * a.Lp * 128;
+  const uint16_t* vtp = a.vt + (int64_t)kvh * a.Lp * 128;
+
+  const int64_t r0 = q0 + 32 * wave;  // first query row of this wave
+  const int64_t my_q = r0 + l32;
+
+  // Q as the B operand of S^T = K Q^T: lane holds query my_q, d = 16ks+8g..+7
+  u32x4 qreg[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    qreg[ks] = *reinterpret_cast<const u32x4*>(qp + my_q * 128 + ks * 16 + g * 8);
+
+  const int64_t kv_end = (q0 + BM < a.L) ? q0 + BM : a.L;
+  const int n_kt = (int)((kv_end + BN - 1) / BN);
+
+  u32x4 pk[4], pv[4];
+  auto load_kv = [&](int kt) {
+    const int64_t k0 = (int64_t)kt * BN;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + 256 * i;
+      int row = c >> 4, cc = c & 15;
+      pk[i] = *reinterpret_cast<const u32x4*>(kp + (k0 + row) * 128 + cc * 8);
+      int dd = c >> 3, vc = c & 7;
+      pv[i] = *reinterpret_cast<const u32x4*>(vtp + (int64_t)dd * a.Lp + k0 + vc * 8);
+    }
+  };
+  auto store_kv = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + 256 * i;
+      int row = c >> 4, cc = c & 15;
+      *reinterpret_cast<u32x4*>(&Ks[buf][row * KP + cc * 8]) = pk[i];
+      int dd = c >> 3, vc = c & 7;
+      *reinterpret_cast<u32x4*>(&Vs[buf][dd * VP + vc * 8]) = pv[i];
+    }
+  };
+
+  f32x16 acc_o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+  const float c = a.scale_log2;
+
+  load_kv(0);
+  store_kv(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < n_kt) load_kv(kt + 1);
+    const int64_t kstart = (int64_t)kt * BN;
+    if (kstart <= r0 + 31) {  // otherwise every key of the tile is in this wave's future
+      const bool need_mask = kstart + BN - 1 > r0;
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        const uint16_t* kbase = &Ks[cur][(kb * 32 + l32) * KP + g * 8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          u32x4 av = *reinterpret_cast<const u32x4*>(kbase + ks * 16);
+          s[kb] = mfma32(av, qreg[ks], s[kb]);
+        }
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            int64_t key = kstart + kb * 32 + acc_row(r, g);
+            if (key > my_q) s[kb][r] = -__builtin_inff();
+          }
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      const float mc = m_new * c;
+      float rsum = 0.f;
+      u32x4 pb[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mc));
+          rsum += p[r];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          pb[kb * 2 + h][0] = pack_bf16x2(p[8 * h + 0], p[8 * h + 1]);
+          pb[kb * 2 + h][1] = pack_bf16x2(p[8 * h + 2], p[8 * h + 3]);
+          pb[kb * 2 + h][2] = pack_bf16x2(p[8 * h + 4], p[8 * h + 5]);
+          pb[kb * 2 + h][3] = pack_bf16x2(p[8 * h + 6], p[8 * h + 7]);
+        }
+      }
+      l_run = l_run * alpha + rsum;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc_o[db] *= alpha;
+      // O^T += V^T P^T; B slot t of step st is key 16*st + 8*(t/4) + 4*g + t%4
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const uint16_t* vb = &Vs[cur][(db * 32 + l32) * VP + st * 16 + g * 4];
+          u32x2 lo = *reinterpret_cast<const u32x2*>(vb);
+          u32x2 hi = *reinterpret_cast<const u32x2*>(vb + 8);
+          u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+          acc_o[db] = mfma32(av, pb[st], acc_o[db]);
+        }
+      }
+    }
+    if (kt + 1 < n_kt) store_kv(cur ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (my_q >= a.L) return;
+  const float inv = 1.f / l_tot;
+  const int hg = a.q_head0 + head;
+  uint16_t* orow = a.o + my_q * a.o_ld + (int64_t)hg * 128;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int d = db * 32 + j * 8 + g * 4;
+      u32x2 w = {pack_bf16x2(acc_o[db][4 * j] * inv, acc_o[db][4 * j + 1] * inv),
+                 pack_bf16x2(acc_o[db][4 * j + 2] * inv, acc_o[db][4 * j + 3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + d) = w;
+    }
+  if (g == 0) a.lse[(int64_t)hg * a.L + my_q] = (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_flash_fwd(const FwdArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.Lp / BM) * a.nh));
+  hipLaunchKernelGGL(flash_fwd_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace upipe

@@ -1,0 +1,134 @@
+// Host-side launch interface of the gfx950 kernels (internal to the library;
+// the public ABI is include/upipe_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace upipe {
+
+// ------------------------------------------------------------------ GEMM
+// C[m][n] = sum_k A(m,k) B(k,n) with bf16 operands and fp32 accumulation.
+//   A(m,k) = A[m*lda + k]  (a_kmajor)   or  A[k*lda + m]
+//   B(k,n) = Brow(n)[k]    (b_kmajor)   or  Brow(k)[n]
+// where Brow(r) = B + map(r)*ldb and map() sends a logical B row (n when
+// b_kmajor, k otherwise) through up to three contiguous segments; this is how
+// a head chunk picks its rows of W_qkv without a copy.
+struct RowSegments {
+  int count;           // 0 = identity map
+  int end[3];          // exclusive logical end of each segment (ascending)
+  int64_t row0[3];     // memory row of the segment's first logical row
+};
+
+enum GemmLayout { GEMM_NT = 0, GEMM_NN = 1, GEMM_TN = 2 };
+enum GemmEpilogue { EPI_STORE_BF16 = 0, EPI_ACCUM_BF16 = 1, EPI_ATOMIC_F32 = 2 };
+
+struct GemmArgs {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  RowSegments bseg;
+  void* C;            // bf16 [M][ldc], or an fp32 [M][N] accumulator (split-K atomics)
+  int64_t ldc;
+  int M, N, K;        // N % 128 == 0; a_kmajor: K % 64 == 0; !a_kmajor: M % 128 == 0
+  int k_per_split;    // multiple of 64; gridDim.z = ceil(K / k_per_split)
+};
+
+hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, hipStream_t s);
+
+// fp32 accumulator [M][N] -> bf16 dst rows dst[map(m)*ld_dst + n]; clears the
+// accumulator for the next split-K GEMM.
+hipError_t launch_acc_to_bf16(float* acc, int M, int N, uint16_t* dst, int64_t ld_dst,
+                              const RowSegments& rows, hipStream_t s);
+
+// ---------------------------------------------------------------- prep
+// Copies heads into the attention kernels' head-major layout, padded with
+// zero rows to Lp, rotating q and k heads (RoPE) on the way.
+struct PrepArgs {
+  const uint16_t* src_q;   // head j of each kind starts at src + j*128; rows every src_ld
+  const uint16_t* src_k;
+  const uint16_t* src_v;
+  int64_t src_ld;
+  int nq, nkv;
+  uint16_t* q_rm;          // [nq][Lp][128]   (may be null)
+  uint16_t* q_t;           // [nq][128][Lp]   (may be null)
+  uint16_t* k_rm;          // [nkv][Lp][128]
+  uint16_t* k_t;           // [nkv][128][Lp]
+  uint16_t* v_rm;          // [nkv][Lp][128]
+  uint16_t* v_t;           // [nkv][128][Lp]
+  int64_t L, Lp;
+};
+hipError_t launch_prep_qkv(const PrepArgs& a, const RopeTable& t, hipStream_t s);
+
+// dO prep for the backward: head-major dO and dO^T, D_i = dO_i . O_i and the
+// base-2 log-sum-exp of each row, all padded to Lp.
+struct PrepDoutArgs {
+  const uint16_t* src_do;  // head j at src_do + j*128, row stride do_ld
+  int64_t do_ld;
+  const uint16_t* o;       // head j at o + j*128, row stride o_ld
+  int64_t o_ld;
+  const float* lse;        // head j at lse + j*L
+  int nh;
+  uint16_t* do_rm;         // [nh][Lp][128]
+  uint16_t* do_t;          // [nh][128][Lp]
+  float* lse2;             // [nh][Lp]
+  float* dvec;             // [nh][Lp]
+  int64_t L, Lp;
+};
+hipError_t launch_prep_dout(const PrepDoutArgs& a, hipStream_t s);
+
+// dq_acc [nh][Lp][128] fp32 -> scale, inverse RoPE -> bf16 dst + row*ld + j*128;
+// clears dq_acc afterwards.
+hipError_t launch_dq_finalize(float* dq_acc, int nh, int64_t L, int64_t Lp, float scale,
+                              uint16_t* dst, int64_t ld, const RopeTable& t, hipStream_t s);
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+// ---------------------------------------------------------- attention
+struct FwdArgs {
+  const uint16_t* q;    // [nh][Lp][128], rotated
+  const uint16_t* k;    // [nkv][Lp][128], rotated
+  const uint16_t* vt;   // [nkv][128][Lp]
+  int nh;               // query heads in this chunk
+  int group;            // G = Hq / Hkv
+  int q_head0;          // global index of the chunk's first q head
+  int kv_head0;         // global index of kv buffer 0
+  uint16_t* o;          // o_saved [L][o_ld]; head h at column h*128
+  int64_t o_ld;
+  float* lse;           // [Hq][L]
+  int64_t L, Lp;
+  float scale_log2;     // log2(e) / sqrt(d)
+};
+hipError_t launch_flash_fwd(const FwdArgs& a, hipStream_t s);
+
+struct BwdArgs {
+  const uint16_t* q;     // [nh][Lp][128] rotated
+  const uint16_t* qt;    // [nh][128][Lp]
+  const uint16_t* k;     // [nkv][Lp][128] rotated
+  const uint16_t* kt;    // [nkv][128][Lp]
+  const uint16_t* v;     // [nkv][Lp][128]
+  const uint16_t* dO;    // [nh][Lp][128]
+  const uint16_t* dOt;   // [nh][128][Lp]
+  const float* lse2;     // [nh][Lp]
+  const float* dvec;     // [nh][Lp]
+  float* dq_acc;         // [nh][Lp][128] fp32, atomically accumulated
+  float* dk_acc;         // [nkv][Lp][128] fp32 cross-chunk accumulators (null if unused)
+  float* dv_acc;
+  int kv_first, kv_last; // this chunk starts / finishes its KV groups
+  uint16_t* dk_out;      // bf16 rows: dk of kv j at dk_out + row*out_ld + j*128 (when kv_last)
+  uint16_t* dv_out;
+  int64_t out_ld;
+  int nh, nkv;
+  int group;             // G
+  int q_head0, kv_head0; // global indices (q head h uses kv head h / G)
+  int64_t L, Lp;
+  float scale_log2;      // log2(e)/sqrt(d)
+  float scale;           // 1/sqrt(d)
+  RopeTable rope;
+};
+hipError_t launch_flash_bwd(const BwdArgs& a, hipStream_t s);
+
+}  // namespace upipe

@@ -1,0 +1,135 @@
+/*
+ * upipe_attn.h - C ABI of the headwise-chunked causal GQA attention layer
+ * (UPipe, "Untied Ulysses") on one MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * One GPU's share of a context-parallel attention layer: full-sequence causal
+ * self-attention over this GPU's Hq query heads and Hkv key/value heads,
+ * processed one head chunk at a time.  Per chunk of `head_chunk` query heads:
+ * the chunk's rows of W_qkv project q (and k, v when a KV group is first
+ * touched), RoPE rotates q and k, causal attention runs, the per-head output
+ * is stored, and the chunk's columns of W_o accumulate into y.  The buffers
+ * for q/k/v and all intermediates are carved from one caller-owned workspace
+ * that every chunk reuses, so workspace grows with head_chunk, not with Hq.
+ *   - method: "Untied Ulysses Pushes Llama-3-8B Training to 5 Million Tokens",
+ *     Untied Ulysses section (one group of heads at a time, a partial result
+ *     stored per group, buffers reused; tailored to grouped-query attention)
+ *     and its chunk-size ablation paragraph (chunk size trades memory for
+ *     throughput; pick the chunk that fits the memory budget);
+ *   - exact attention: "Untied Ulysses: Memory-Efficient Context Parallelism
+ *     via Headwise Chunking", Abstract and Builds-on list (Attention Is All You
+ *     Need, RoFormer, FlashAttention).
+ * Conventions where the pages are silent: scale 1/sqrt(head_dim); query i sees
+ * keys j <= i; q head h uses KV head h / (Hq/Hkv); W_qkv rows are packed
+ * [Q heads | K heads | V heads], head_dim rows per head, no bias (nn.Linear
+ * [out, in] layout); W_o is [hidden, Hq*head_dim]; RoPE rotates consecutive
+ * pairs (2i, 2i+1) by p * theta^(-2i/head_dim) at position p = 0..L-1.
+ *
+ * Common argument rules (every entry point)
+ * -----------------------------------------
+ *  - All tensor pointers are DEVICE memory owned by the caller; the library
+ *    never allocates or frees device memory and keeps no pointer after return.
+ *  - bfloat16 tensors are passed as uint16_t bit patterns, row-major and
+ *    contiguous; every pointer must be 16-byte aligned, the workspace
+ *    256-byte aligned.
+ *  - Batch is 1 and attention is causal.
+ *  - hidden == 0 selects q/k/v-given mode: x is packed q|k|v
+ *    [L, (Hq+2Hkv)*head_dim] (already projected, not yet rotated), the
+ *    weights and y / dw_* must be NULL, dy is dO [L, Hq*head_dim] and dx is
+ *    dqkv [L, (Hq+2Hkv)*head_dim].
+ *  - Supported: head_dim == 128, hidden a multiple of 128 (or 0),
+ *    1 <= L <= 2^24, Hq % Hkv == 0, Hq % head_chunk == 0 and either
+ *    head_chunk % G == 0 or G % head_chunk == 0 (G = Hq/Hkv), so that no chunk
+ *    holds part of two KV groups' query heads.
+ *  - All checks run on the host before the first launch; on any error nothing
+ *    is launched and outputs are untouched.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ *    null stream) and is asynchronous: the call returns before the GPU is
+ *    done.  The library never synchronizes.  Calls that share a workspace
+ *    must be ordered on one stream.
+ *  - Outputs are fully overwritten (never accumulated into).
+ */
+#ifndef UPIPE_ATTN_H
+#define UPIPE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define UPIPE_OK 0
+#define UPIPE_EINVAL (-1)       /* bad size, count, or pointer combination        */
+#define UPIPE_EUNSUPPORTED (-2) /* head_dim != 128, hidden % 128 != 0, L > 2^24   */
+#define UPIPE_ECHUNK (-3)       /* head_chunk does not divide Hq or straddles a KV group */
+#define UPIPE_EWORKSPACE (-4)   /* workspace NULL, misaligned or smaller than required */
+#define UPIPE_EHIP (-5)         /* the HIP runtime reported an error at launch    */
+
+#define UPIPE_PASS_FWD 0
+#define UPIPE_PASS_BWD 1
+
+/*
+ * Workspace size query.  Writes to *bytes the workspace that upipe_attn_fwd
+ * (pass = UPIPE_PASS_FWD) or upipe_attn_bwd (pass = UPIPE_PASS_BWD) needs for
+ * these shapes.  The size is affine in head_chunk (per-chunk q-side buffers
+ * plus the resident KV group): choosing head_chunk is how a caller fits the
+ * layer into its memory budget (chunk-size ablation paragraph of the
+ * talk write-up).  Returns UPIPE_OK or the error the entry point itself would
+ * return for these shapes.  Host only; touches no GPU.
+ */
+int upipe_attn_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, int32_t head_chunk,
+                               int32_t pass, size_t* bytes);
+
+/*
+ * Forward pass.
+ *  x        [L, hidden] bf16 (projection mode) or packed q|k|v (hidden == 0)
+ *  w_qkv    [(Hq+2Hkv)*head_dim, hidden] bf16, NULL iff hidden == 0
+ *  w_o      [hidden, Hq*head_dim] bf16, NULL iff hidden == 0
+ *  y        [L, hidden] bf16 out, NULL iff hidden == 0
+ *  o_saved  [L, Hq*head_dim] bf16 out: per-head attention output (before W_o);
+ *           upipe_attn_bwd reads it back
+ *  lse      [Hq, L] fp32 out: natural-log sum of exp of the scaled scores of
+ *           each query row; upipe_attn_bwd reads it back
+ *  workspace, workspace_bytes: caller-owned scratch of at least the size the
+ *           query returns for UPIPE_PASS_FWD; contents on entry are ignored
+ *  stream   hipStream_t or NULL
+ */
+int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
+                   int32_t head_dim, double rope_theta, int32_t head_chunk,
+                   const uint16_t* x, const uint16_t* w_qkv, const uint16_t* w_o,
+                   uint16_t* y, uint16_t* o_saved, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass (chain rule of the forward; q/k/v are recomputed per chunk
+ * from x, so only o_saved and lse are kept from the forward).
+ *  x, w_qkv, w_o   as in upipe_attn_fwd
+ *  o_saved, lse    the forward's outputs for the same inputs
+ *  dy       [L, hidden] bf16 upstream gradient of y, or dO [L, Hq*head_dim]
+ *  dx       [L, hidden] bf16 out, or dqkv [L, (Hq+2Hkv)*head_dim] (hidden == 0)
+ *  dw_qkv   [(Hq+2Hkv)*head_dim, hidden] bf16 out, NULL iff hidden == 0
+ *  dw_o     [hidden, Hq*head_dim] bf16 out, NULL iff hidden == 0
+ *  workspace, workspace_bytes: at least the UPIPE_PASS_BWD query size
+ */
+int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
+                   int32_t head_dim, double rope_theta, int32_t head_chunk,
+                   const uint16_t* x, const uint16_t* w_qkv, const uint16_t* w_o,
+                   const uint16_t* o_saved, const float* lse, const uint16_t* dy,
+                   uint16_t* dx, uint16_t* dw_qkv, uint16_t* dw_o,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a status code.  Never NULL. */
+const char* upipe_strerror(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int upipe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UPIPE_ATTN_H */

@@ -1,0 +1,170 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+declared entry point, and every argument check returns its status before any
+HIP call; the workspace planner is affine in the head chunk."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import headwise_chunked_context_amd as hc_amd
+from headwise_chunked_context_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "upipe_attn.h")
+
+# fake, 256-byte aligned device addresses: never dereferenced by the host
+P = 0x7F0000000000
+WS = 0x7F1000000000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(upipe_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = hc_amd.lib()
+    names = _declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.upipe_version() >= 100
+
+
+def test_strerror_covers_every_status():
+    seen = set()
+    for code in (0, -1, -2, -3, -4, -5):
+        msg = hc_amd.strerror(code)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert hc_amd.strerror(12345) == "unknown status"
+
+
+def _ws(L, D, nq, nkv, d, hc, pss):
+    out = ctypes.c_size_t(0)
+    rc = hc_amd.lib().upipe_attn_workspace_bytes(L, D, nq, nkv, d, hc, pss, ctypes.byref(out))
+    return rc, out.value
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1024, 1024, 8, 2, 128, 2, 0), B.UPIPE_OK),
+    ((0, 1024, 8, 2, 128, 2, 0), B.UPIPE_EINVAL),            # L = 0
+    ((-5, 1024, 8, 2, 128, 2, 0), B.UPIPE_EINVAL),
+    ((1024, -128, 8, 2, 128, 2, 0), B.UPIPE_EINVAL),
+    ((1024, 1024, 8, 3, 128, 2, 0), B.UPIPE_EINVAL),         # Hq % Hkv
+    ((1024, 1024, 0, 1, 128, 1, 0), B.UPIPE_EINVAL),
+    ((1024, 1024, 8, 2, 64, 2, 0), B.UPIPE_EUNSUPPORTED),    # head_dim
+    ((1024, 1000, 8, 2, 128, 2, 0), B.UPIPE_EUNSUPPORTED),   # hidden % 128
+    (((1 << 24) + 1, 0, 4, 1, 128, 1, 0), B.UPIPE_EUNSUPPORTED),
+    ((1024, 1024, 8, 2, 128, 3, 0), B.UPIPE_ECHUNK),         # does not divide Hq
+    ((1024, 1536, 12, 3, 128, 6, 1), B.UPIPE_ECHUNK),        # G = 4, chunk 6 straddles
+    ((1024, 1024, 8, 2, 128, 0, 0), B.UPIPE_EINVAL),
+    ((1024, 1024, 8, 2, 128, 2, 7), B.UPIPE_EINVAL),         # bad pass
+])
+def test_workspace_query_status(args, code):
+    rc, _ = _ws(*args)
+    assert rc == code
+
+
+def test_workspace_query_null_output():
+    rc = hc_amd.lib().upipe_attn_workspace_bytes(1024, 1024, 8, 2, 128, 2, 0, None)
+    assert rc == B.UPIPE_EINVAL
+
+
+@pytest.mark.parametrize("pss", [B.PASS_FWD, B.PASS_BWD])
+@pytest.mark.parametrize("shape", [(262144, 5120, 8, 1), (524288, 0, 4, 1), (32768, 4096, 32, 8)])
+def test_workspace_affine_and_shrinking_in_chunk(shape, pss):
+    L, D, nq, nkv = shape
+    G = nq // nkv
+    chunks = [c for c in (1, 2, 4, 8, 16, 32) if nq % c == 0 and (c % G == 0 or G % c == 0)]
+    sizes = {c: _ws(L, D, nq, nkv, 128, c, pss)[1] for c in chunks}
+    for a, b in zip(chunks, chunks[1:]):
+        assert sizes[a] < sizes[b]
+    # affine within each regime: chunks below the group size touch one KV head,
+    # chunks of whole groups touch c/G KV heads (still linear in c)
+    lo = [c for c in chunks if c <= G]
+    hi = [c for c in chunks if c >= G]
+    for grp in (lo, hi):
+        if len(grp) >= 3:
+            slopes = [(sizes[b] - sizes[a]) / (b - a) for a, b in zip(grp, grp[1:])]
+            assert max(slopes) == min(slopes), slopes
+
+
+def test_query_side_reduction_matches_page_figure():
+    """The 32B-share shape (8 q heads, 1 KV head per GPU) at chunk 1 keeps
+    1/8 of the per-query-head workspace it needs at chunk 8."""
+    fig = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
+    want = fig["attention_intermediate_reduction_32b"]["value"]
+    L, D = 262144, 5120
+    for pss in (B.PASS_FWD, B.PASS_BWD):
+        s = {c: _ws(L, D, 8, 1, 128, c, pss)[1] for c in (1, 2, 8)}
+        per_head = s[2] - s[1]
+        resident = s[1] - per_head          # the part that does not scale with the chunk
+        q1, q8 = s[1] - resident, s[8] - resident
+        assert abs((1 - q1 / q8) - want) < 1e-12
+    lo, hi = fig["chunk_sizes_ablated"]["value"]
+    assert _ws(L, D, 32, 1, 128, lo, 0)[1] < _ws(L, D, 32, 1, 128, hi, 0)[1]
+
+
+def _fwd(**kw):
+    a = dict(L=1024, D=1024, nq=8, nkv=2, d=128, theta=5e5, hc=2,
+             x=P, wqkv=P, wo=P, y=P, o=P, lse=P, ws=WS, wsb=1 << 40)
+    a.update(kw)
+    return hc_amd.lib().upipe_attn_fwd(a["L"], a["D"], a["nq"], a["nkv"], a["d"], a["theta"],
+                                       a["hc"], a["x"], a["wqkv"], a["wo"], a["y"], a["o"],
+                                       a["lse"], a["ws"], a["wsb"], None)
+
+
+def _bwd(**kw):
+    a = dict(L=1024, D=1024, nq=8, nkv=2, d=128, theta=5e5, hc=2, x=P, wqkv=P, wo=P, o=P,
+             lse=P, dy=P, dx=P, dwqkv=P, dwo=P, ws=WS, wsb=1 << 40)
+    a.update(kw)
+    return hc_amd.lib().upipe_attn_bwd(a["L"], a["D"], a["nq"], a["nkv"], a["d"], a["theta"],
+                                       a["hc"], a["x"], a["wqkv"], a["wo"], a["o"], a["lse"],
+                                       a["dy"], a["dx"], a["dwqkv"], a["dwo"], a["ws"], a["wsb"],
+                                       None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), B.UPIPE_EINVAL),
+    (dict(wo=None), B.UPIPE_EINVAL),                 # projection mode needs both weights
+    (dict(y=None), B.UPIPE_EINVAL),
+    (dict(o=None), B.UPIPE_EINVAL),
+    (dict(lse=None), B.UPIPE_EINVAL),
+    (dict(x=P + 2), B.UPIPE_EINVAL),                 # misaligned
+    (dict(theta=0.0), B.UPIPE_EINVAL),
+    (dict(theta=float("nan")), B.UPIPE_EINVAL),
+    (dict(ws=None), B.UPIPE_EWORKSPACE),
+    (dict(ws=WS + 16), B.UPIPE_EWORKSPACE),          # not 256-byte aligned
+    (dict(wsb=1024), B.UPIPE_EWORKSPACE),            # too small
+    (dict(hc=3), B.UPIPE_ECHUNK),
+    (dict(d=96), B.UPIPE_EUNSUPPORTED),
+    (dict(D=0, wqkv=None, wo=None), B.UPIPE_EINVAL),  # q/k/v-given mode must not get y
+    (dict(L=0), B.UPIPE_EINVAL),
+])
+def test_fwd_rejects_before_launch(kw, code):
+    assert _fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dy=None), B.UPIPE_EINVAL),
+    (dict(dx=None), B.UPIPE_EINVAL),
+    (dict(dwo=None), B.UPIPE_EINVAL),
+    (dict(D=0, wqkv=None, wo=None), B.UPIPE_EINVAL),   # weight grads must be NULL then
+    (dict(lse=P + 4), B.UPIPE_EINVAL),
+    (dict(wsb=0), B.UPIPE_EWORKSPACE),
+    (dict(nkv=3), B.UPIPE_EINVAL),
+    (dict(hc=16), B.UPIPE_ECHUNK),
+])
+def test_bwd_rejects_before_launch(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_exact_workspace_size_is_accepted_by_the_check():
+    # one byte short of the query is rejected; the check runs before any launch
+    rc, need = _ws(1024, 1024, 8, 2, 128, 2, B.PASS_BWD)
+    assert rc == 0 and need > 0
+    assert _bwd(wsb=need - 1) == B.UPIPE_EWORKSPACE
