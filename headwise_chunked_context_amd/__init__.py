@@ -5,6 +5,7 @@ include/upipe_attn.h); this package is its thin ctypes binding.
 """
 from .binding import (  # noqa: F401
     EXPORTS,
+    KERNEL_KINDS,
     PASS_BWD,
     PASS_FWD,
     UPIPE_ECHUNK,
@@ -17,6 +18,8 @@ from .binding import (  # noqa: F401
     attn_bwd,
     attn_fwd,
     lib,
+    profile_enable,
+    profile_read,
     strerror,
     workspace_bytes,
 )

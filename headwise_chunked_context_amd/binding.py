@@ -27,9 +27,13 @@ EXPORTS = (
     "upipe_attn_workspace_bytes",
     "upipe_attn_fwd",
     "upipe_attn_bwd",
+    "upipe_profile_enable",
+    "upipe_profile_read",
     "upipe_strerror",
     "upipe_version",
 )
+
+KERNEL_KINDS = {"attn_fwd": 0, "attn_bwd": 1, "gemm": 2, "prep": 3, "finalize": 4}
 
 
 class UpipeError(RuntimeError):
@@ -65,6 +69,11 @@ def lib() -> ctypes.CDLL:
     L.upipe_strerror.restype = ctypes.c_char_p
     L.upipe_version.argtypes = []
     L.upipe_version.restype = ctypes.c_int
+    L.upipe_profile_enable.argtypes = [ctypes.c_int]
+    L.upipe_profile_enable.restype = ctypes.c_int
+    L.upipe_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int64)]
+    L.upipe_profile_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -81,6 +90,23 @@ def workspace_bytes(L: int, hidden: int, n_q: int, n_kv: int, head_dim: int, hea
     if rc != UPIPE_OK:
         raise UpipeError(rc, "upipe_attn_workspace_bytes")
     return out.value
+
+
+def profile_enable(on: bool) -> None:
+    """Start (clearing old records) or stop per-kernel-class event timing."""
+    lib().upipe_profile_enable(1 if on else 0)
+
+
+def profile_read() -> dict:
+    """{kind: (total_ms, launches)} since the last profile_enable(True)."""
+    out = {}
+    for name, kind in KERNEL_KINDS.items():
+        ms, n = ctypes.c_double(0), ctypes.c_int64(0)
+        rc = lib().upipe_profile_read(kind, ctypes.byref(ms), ctypes.byref(n))
+        if rc != UPIPE_OK:
+            raise UpipeError(rc, "upipe_profile_read")
+        out[name] = (ms.value, n.value)
+    return out
 
 
 def _ptr(t):

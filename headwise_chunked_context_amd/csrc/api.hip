@@ -3,13 +3,16 @@
 //
 // The schedule is the method's: one head chunk at a time, the chunk's rows of
 // W_qkv project its q (and k/v when a KV group is first touched), attention
-// runs, the per-head output is stored and the chunk's share of W_o
-// accumulates into y; the next chunk reuses the same workspace buffers
+// runs and the per-head output is stored as the chunk's partial result; the
+// next chunk reuses the same workspace buffers
 // ("Untied Ulysses Pushes Llama-3-8B Training to 5 Million Tokens", Untied
 // Ulysses section).  A KV group stays resident in the workspace while any of
 // its query heads is being processed (grouped-query tailoring, same section).
 #include <math.h>
 #include <string.h>
+
+#include <utility>
+#include <vector>
 
 #include "../../include/upipe_attn.h"
 #include "kernels.h"
@@ -155,6 +158,40 @@ int check_common(const Shape& s, double theta, const void* x, const void* w_qkv,
     if ((expr) != hipSuccess) return UPIPE_EHIP; \
   } while (0)
 
+// ---- optional per-kernel-class timing (see upipe_profile_enable)
+constexpr int kKinds = 5;
+struct Profiler {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[kKinds];
+  std::vector<hipEvent_t> pool;
+};
+Profiler g_prof;
+
+hipEvent_t prof_event() {
+  if (!g_prof.pool.empty()) {
+    hipEvent_t e = g_prof.pool.back();
+    g_prof.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename F>
+hipError_t timed(int kind, hipStream_t st, F&& launch) {
+  if (!g_prof.on) return launch();
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  if (hipEventRecord(a, st) != hipSuccess) return hipErrorUnknown;
+  hipError_t e = launch();
+  if (hipEventRecord(b, st) != hipSuccess) return hipErrorUnknown;
+  g_prof.rec[kind].push_back({a, b});
+  return e;
+}
+
+#define UPIPE_LAUNCH(kind, expr) UPIPE_TRY(timed((kind), st, [&]() { return (expr); }))
+
 struct Chunk {
   int h0;        // first q head
   int g0;        // first KV group touched
@@ -176,7 +213,7 @@ Chunk chunk_info(const Shape& s, int c) {
 // Stage the chunk's q (and k, v when it starts a group) in GEMM output
 // layout: staging[L][hc*d | kc*d | kc*d].
 int project_chunk(const Shape& s, const Chunk& ch, const uint16_t* x, const uint16_t* w_qkv,
-                  uint16_t* staging, hipStream_t st) {
+                  uint16_t* staging, const RopeTable& rope, hipStream_t st) {
   const int d = s.d;
   const int width = (s.hc + 2 * s.kc) * d;
   GemmArgs g;
@@ -198,7 +235,12 @@ int project_chunk(const Shape& s, const Chunk& ch, const uint16_t* x, const uint
   g.N = ch.kv_first ? width : s.hc * d;
   g.K = s.D;
   g.k_per_split = s.D;
-  UPIPE_TRY(launch_gemm(GEMM_NT, EPI_STORE_BF16, g, st));
+  // q and k leave the GEMM already rotated: one bf16 rounding after RoPE;
+  // v leaves it as fp16 (the forward's P V product takes fp16 operands)
+  g.rope_cols = (s.hc + s.kc) * d;
+  g.f16_from = (s.hc + s.kc) * d;
+  g.rope = rope;
+  UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_NT, EPI_STORE_BF16, g, st));
   return UPIPE_OK;
 }
 
@@ -207,6 +249,32 @@ int project_chunk(const Shape& s, const Chunk& ch, const uint16_t* x, const uint
 extern "C" {
 
 int upipe_version(void) { return 100; }
+
+int upipe_profile_enable(int on) {
+  for (int k = 0; k < kKinds; ++k) {
+    for (auto& pr : g_prof.rec[k]) {
+      g_prof.pool.push_back(pr.first);
+      g_prof.pool.push_back(pr.second);
+    }
+    g_prof.rec[k].clear();
+  }
+  g_prof.on = on != 0;
+  return UPIPE_OK;
+}
+
+int upipe_profile_read(int kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= kKinds || !total_ms || !launches) return UPIPE_EINVAL;
+  double sum = 0.0;
+  for (auto& pr : g_prof.rec[kind]) {
+    if (hipEventSynchronize(pr.second) != hipSuccess) return UPIPE_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return UPIPE_EHIP;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int64_t)g_prof.rec[kind].size();
+  return UPIPE_OK;
+}
 
 const char* upipe_strerror(int status) {
   switch (status) {
@@ -260,7 +328,7 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     PrepArgs pa;
     memset(&pa, 0, sizeof(pa));
     if (s.proj) {
-      rc = project_chunk(s, ch, x, w_qkv, staging, st);
+      rc = project_chunk(s, ch, x, w_qkv, staging, rope, st);
       if (rc != UPIPE_OK) return rc;
       pa.src_q = staging;
       pa.src_k = staging + s.hc * d;
@@ -279,7 +347,10 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pa.v_t = v_t;
     pa.L = s.L;
     pa.Lp = s.Lp;
-    UPIPE_TRY(launch_prep_qkv(pa, rope, st));
+    pa.rotate = s.proj ? 0 : 1;
+    pa.v_src_f16 = s.proj ? 1 : 0;
+    pa.v_out_f16 = 1;
+    UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_qkv(pa, rope, st));
 
     // 2. causal attention of the chunk's heads; stores O and LSE
     FwdArgs fa;
@@ -296,24 +367,27 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     fa.L = s.L;
     fa.Lp = s.Lp;
     fa.scale_log2 = kLog2e / sqrtf((float)d);
-    UPIPE_TRY(launch_flash_fwd(fa, st));
+    UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_FWD, launch_flash_fwd(fa, st));
+  }
 
-    // 3. y (+)= O_c W_o[:, cols(c)]^T
-    if (s.proj) {
-      GemmArgs g;
-      memset(&g, 0, sizeof(g));
-      g.A = o_saved + (int64_t)ch.h0 * d;
-      g.lda = (int64_t)s.Hq * d;
-      g.B = w_o + (int64_t)ch.h0 * d;
-      g.ldb = (int64_t)s.Hq * d;
-      g.C = y;
-      g.ldc = s.D;
-      g.M = (int)s.L;
-      g.N = s.D;
-      g.K = s.hc * d;
-      g.k_per_split = g.K;
-      UPIPE_TRY(launch_gemm(GEMM_NT, c == 0 ? EPI_STORE_BF16 : EPI_ACCUM_BF16, g, st));
-    }
+  // 3. output projection: y = sum over chunks of O_c W_o[:, cols(c)]^T.  The
+  // chunks' partial results are the column blocks of o_saved; the GEMM's K
+  // loop walks them chunk after chunk and accumulates in fp32, so y is
+  // rounded to bf16 once instead of once per chunk.
+  if (s.proj) {
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A = o_saved;
+    g.lda = (int64_t)s.Hq * d;
+    g.B = w_o;
+    g.ldb = (int64_t)s.Hq * d;
+    g.C = y;
+    g.ldc = s.D;
+    g.M = (int)s.L;
+    g.N = s.D;
+    g.K = s.Hq * d;
+    g.k_per_split = g.K;
+    UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_NT, EPI_STORE_BF16, g, st));
   }
   return UPIPE_OK;
 }
@@ -356,8 +430,8 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   float* dw_acc = at<float>(workspace, p.dw_acc);
 
   // accumulators start at zero; each finalize pass clears what it consumed
-  UPIPE_TRY(launch_zero(dq_acc, (size_t)s.hc * s.Lp * d * 4, st));
-  if (dw_acc) UPIPE_TRY(launch_zero(dw_acc, (size_t)width * s.D * 4, st));
+  UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_zero(dq_acc, (size_t)s.hc * s.Lp * d * 4, st));
+  if (dw_acc) UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_zero(dw_acc, (size_t)width * s.D * 4, st));
 
   for (int c = 0; c < s.Hq / s.hc; ++c) {
     const Chunk ch = chunk_info(s, c);
@@ -365,7 +439,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     PrepArgs pa;
     memset(&pa, 0, sizeof(pa));
     if (s.proj) {
-      rc = project_chunk(s, ch, x, w_qkv, staging, st);
+      rc = project_chunk(s, ch, x, w_qkv, staging, rope, st);
       if (rc != UPIPE_OK) return rc;
       pa.src_q = staging;
       pa.src_k = staging + s.hc * d;
@@ -386,7 +460,10 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pa.v_rm = v_rm;
     pa.L = s.L;
     pa.Lp = s.Lp;
-    UPIPE_TRY(launch_prep_qkv(pa, rope, st));
+    pa.rotate = s.proj ? 0 : 1;
+    pa.v_src_f16 = s.proj ? 1 : 0;
+    pa.v_out_f16 = 0;
+    UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_qkv(pa, rope, st));
 
     // 2. dO of the chunk's heads (dy W_o[:, cols] or the given dO) and dW_o
     PrepDoutArgs pd;
@@ -413,7 +490,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       g.N = s.hc * d;
       g.K = s.D;
       g.k_per_split = s.D;
-      UPIPE_TRY(launch_gemm(GEMM_NN, EPI_STORE_BF16, g, st));
+      UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_NN, EPI_STORE_BF16, g, st));
       pd.src_do = staging;
       pd.do_ld = s.hc * d;
 
@@ -430,16 +507,16 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       w.N = s.hc * d;
       w.K = (int)s.L;
       w.k_per_split = k_per_split(s.L, splits);
-      UPIPE_TRY(launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, st));
+      UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, st));
       RowSegments ident;
       memset(&ident, 0, sizeof(ident));
-      UPIPE_TRY(launch_acc_to_bf16(dw_acc, s.D, s.hc * d, dw_o + (int64_t)ch.h0 * d,
+      UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_acc_to_bf16(dw_acc, s.D, s.hc * d, dw_o + (int64_t)ch.h0 * d,
                                    (int64_t)s.Hq * d, ident, st));
     } else {
       pd.src_do = dy + (int64_t)ch.h0 * d;
       pd.do_ld = (int64_t)s.Hq * d;
     }
-    UPIPE_TRY(launch_prep_dout(pd, st));
+    UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_dout(pd, st));
 
     // 3. attention backward: dQ into the fp32 accumulator, dK/dV of the groups
     BwdArgs ba;
@@ -481,8 +558,8 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     ba.scale_log2 = kLog2e / sqrtf((float)d);
     ba.scale = 1.f / sqrtf((float)d);
     ba.rope = rope;
-    UPIPE_TRY(launch_flash_bwd(ba, st));
-    UPIPE_TRY(launch_dq_finalize(dq_acc, s.hc, s.L, s.Lp, ba.scale, grad_base, grad_ld, rope, st));
+    UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_BWD, launch_flash_bwd(ba, st));
+    UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_dq_finalize(dq_acc, s.hc, s.L, s.Lp, ba.scale, grad_base, grad_ld, rope, st));
 
     // 4. dx (+)= [dq | dk | dv] W_qkv[rows], dW_qkv[rows] = [dq | dk | dv]^T x
     if (s.proj) {
@@ -510,7 +587,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       g.N = s.D;
       g.K = ncols;
       g.k_per_split = ncols;
-      UPIPE_TRY(launch_gemm(GEMM_NN, c == 0 ? EPI_STORE_BF16 : EPI_ACCUM_BF16, g, st));
+      UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_NN, c == 0 ? EPI_STORE_BF16 : EPI_ACCUM_BF16, g, st));
 
       const int splits = dw_splits(s.L, ncols, s.D);
       GemmArgs w;
@@ -524,8 +601,8 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       w.N = s.D;
       w.K = (int)s.L;
       w.k_per_split = k_per_split(s.L, splits);
-      UPIPE_TRY(launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, st));
-      UPIPE_TRY(launch_acc_to_bf16(dw_acc, ncols, s.D, dw_qkv, s.D, seg, st));
+      UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, st));
+      UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_acc_to_bf16(dw_acc, ncols, s.D, dw_qkv, s.D, seg, st));
     }
   }
   return UPIPE_OK;

@@ -202,6 +202,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     f32x4 lo = *reinterpret_cast<const f32x4*>(src);
     f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
     u32x4* dst = reinterpret_cast<u32x4*>(C + (int64_t)m * p.ldc + n0 + cc * 8);
+    if (EPI == EPI_STORE_BF16 && n0 + cc * 8 < p.rope_cols) {
+      // RoPE in fp32 on the four pairs of this 8-column chunk, position m
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const int pair0 = ((n0 + cc * 8) & 127) >> 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float c, s;
+        rope_cos_sin(p.rope, m, pair0 + j, c, s);
+        float e = v[2 * j], o = v[2 * j + 1];
+        v[2 * j] = e * c - o * s;
+        v[2 * j + 1] = e * s + o * c;
+      }
+      lo = f32x4{v[0], v[1], v[2], v[3]};
+      hi = f32x4{v[4], v[5], v[6], v[7]};
+    }
     if (EPI == EPI_ACCUM_BF16) {
       u32x4 old = *dst;
       lo[0] += bf16_lo(old[0]); lo[1] += bf16_hi(old[0]);
@@ -210,10 +225,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
       hi[2] += bf16_lo(old[3]); hi[3] += bf16_hi(old[3]);
     }
     u32x4 out;
-    out[0] = pack_bf16x2(lo[0], lo[1]);
-    out[1] = pack_bf16x2(lo[2], lo[3]);
-    out[2] = pack_bf16x2(hi[0], hi[1]);
-    out[3] = pack_bf16x2(hi[2], hi[3]);
+    if (EPI == EPI_STORE_BF16 && p.f16_from > 0 && n0 + cc * 8 >= p.f16_from) {
+      out[0] = pack_f16x2_sat(lo[0], lo[1]);
+      out[1] = pack_f16x2_sat(lo[2], lo[3]);
+      out[2] = pack_f16x2_sat(hi[0], hi[1]);
+      out[3] = pack_f16x2_sat(hi[2], hi[3]);
+    } else {
+      out[0] = pack_bf16x2(lo[0], lo[1]);
+      out[1] = pack_bf16x2(lo[2], lo[3]);
+      out[2] = pack_bf16x2(hi[0], hi[1]);
+      out[3] = pack_bf16x2(hi[2], hi[3]);
+    }
     *dst = out;
   }
 }

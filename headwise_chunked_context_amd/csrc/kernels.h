@@ -35,6 +35,13 @@ struct GemmArgs {
   int64_t ldc;
   int M, N, K;        // N % 128 == 0; a_kmajor: K % 64 == 0; !a_kmajor: M % 128 == 0
   int k_per_split;    // multiple of 64; gridDim.z = ceil(K / k_per_split)
+  // bf16 store epilogue only: output columns n < rope_cols are rotated (RoPE,
+  // position = row m, pair = (n % 128) / 2) in fp32 before the one rounding
+  int rope_cols;
+  // bf16 store epilogue only: if > 0, output columns n >= f16_from are stored
+  // as fp16 (saturated to +-65504) instead of bf16
+  int f16_from;
+  RopeTable rope;
 };
 
 hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, hipStream_t s);
@@ -46,7 +53,8 @@ hipError_t launch_acc_to_bf16(float* acc, int M, int N, uint16_t* dst, int64_t l
 
 // ---------------------------------------------------------------- prep
 // Copies heads into the attention kernels' head-major layout, padded with
-// zero rows to Lp, rotating q and k heads (RoPE) on the way.
+// zero rows to Lp, rotating q and k heads (RoPE) on the way unless the
+// source is already rotated (the projection GEMM rotates in its epilogue).
 struct PrepArgs {
   const uint16_t* src_q;   // head j of each kind starts at src + j*128; rows every src_ld
   const uint16_t* src_k;
@@ -60,6 +68,9 @@ struct PrepArgs {
   uint16_t* v_rm;          // [nkv][Lp][128]
   uint16_t* v_t;           // [nkv][128][Lp]
   int64_t L, Lp;
+  int rotate;              // apply RoPE to q and k heads
+  int v_src_f16;           // v source holds fp16 bits (else bf16)
+  int v_out_f16;           // write v_rm / v_t as fp16 (else bf16)
 };
 hipError_t launch_prep_qkv(const PrepArgs& a, const RopeTable& t, hipStream_t s);
 
@@ -91,7 +102,7 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 struct FwdArgs {
   const uint16_t* q;    // [nh][Lp][128], rotated
   const uint16_t* k;    // [nkv][Lp][128], rotated
-  const uint16_t* vt;   // [nkv][128][Lp]
+  const uint16_t* vt;   // [nkv][128][Lp] fp16
   int nh;               // query heads in this chunk
   int group;            // G = Hq / Hkv
   int q_head0;          // global index of the chunk's first q head

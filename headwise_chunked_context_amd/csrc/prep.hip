@@ -1,7 +1,8 @@
 // Memory-bound passes around the attention kernels (gfx950):
 //   prep_qkv    head-major copies of a chunk's q/k/v, RoPE on q and k,
 //               optional transposed copies (d-major) for the MFMA operands
-//               that contract over the sequence, zero padding to Lp rows;
+//               that contract over the sequence, zero padding to Lp rows,
+//               v converted between bf16 and fp16 as the consumer needs;
 //   prep_dout   the same for dO, plus D_i = dO_i . O_i and LSE in base 2;
 //   dq_finalize fp32 dQ accumulator -> scaled, inverse-rotated bf16;
 //   zero        fill kernel (used instead of hipMemsetAsync).
@@ -37,17 +38,18 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a, RopeTable t) 
   const uint16_t* src;
   uint16_t *rm, *tr;
   bool rot;
+  const bool is_v = slot >= a.nq + a.nkv;
   if (slot < a.nq) {
     src = a.src_q + slot * 128;
     rm = a.q_rm ? a.q_rm + (int64_t)slot * a.Lp * 128 : nullptr;
     tr = a.q_t ? a.q_t + (int64_t)slot * a.Lp * 128 : nullptr;
-    rot = true;
+    rot = a.rotate != 0;
   } else if (slot < a.nq + a.nkv) {
     int j = slot - a.nq;
     src = a.src_k + j * 128;
     rm = a.k_rm ? a.k_rm + (int64_t)j * a.Lp * 128 : nullptr;
     tr = a.k_t ? a.k_t + (int64_t)j * a.Lp * 128 : nullptr;
-    rot = true;
+    rot = a.rotate != 0;
   } else {
     int j = slot - a.nq - a.nkv;
     src = a.src_v + j * 128;
@@ -65,6 +67,13 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a, RopeTable t) 
     if (row < a.L) {
       v = *reinterpret_cast<const u32x4*>(src + row * a.src_ld + cc * 8);
       if (rot) v = rotate8(v, t, row, cc * 4, false);
+      if (is_v && a.v_src_f16 && !a.v_out_f16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(f16_lo(v[j]), f16_hi(v[j]));
+      } else if (is_v && !a.v_src_f16 && a.v_out_f16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = pack_f16x2_sat(bf16_lo(v[j]), bf16_hi(v[j]));
+      }
     }
     if (rm) *reinterpret_cast<u32x4*>(rm + row * 128 + cc * 8) = v;
     if (tr) {

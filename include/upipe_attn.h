@@ -8,10 +8,13 @@
  * self-attention over this GPU's Hq query heads and Hkv key/value heads,
  * processed one head chunk at a time.  Per chunk of `head_chunk` query heads:
  * the chunk's rows of W_qkv project q (and k, v when a KV group is first
- * touched), RoPE rotates q and k, causal attention runs, the per-head output
- * is stored, and the chunk's columns of W_o accumulate into y.  The buffers
- * for q/k/v and all intermediates are carved from one caller-owned workspace
- * that every chunk reuses, so workspace grows with head_chunk, not with Hq.
+ * touched), RoPE rotates q and k, causal attention runs and the chunk's
+ * per-head output (its partial result) is stored in o_saved.  After the last
+ * chunk the output projection accumulates every chunk's partial result
+ * through its columns of W_o into y (fp32 accumulation, one bf16 rounding).
+ * The buffers for q/k/v and all intermediates are carved from one
+ * caller-owned workspace that every chunk reuses, so workspace grows with
+ * head_chunk, not with Hq.
  *   - method: "Untied Ulysses Pushes Llama-3-8B Training to 5 Million Tokens",
  *     Untied Ulysses section (one group of heads at a time, a partial result
  *     stored per group, buffers reused; tailored to grouped-query attention)
@@ -121,6 +124,30 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
                    const uint16_t* o_saved, const float* lse, const uint16_t* dy,
                    uint16_t* dx, uint16_t* dw_qkv, uint16_t* dw_o,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Kernel timing for measurement tools (not needed to use the layer).
+ * upipe_profile_enable(1) clears previous records and, until
+ * upipe_profile_enable(0), brackets every kernel launch of upipe_attn_fwd /
+ * upipe_attn_bwd with a pair of HIP events recorded on the caller's stream.
+ * upipe_profile_read(kind, ...) waits for the recorded events and returns the
+ * summed GPU milliseconds and the number of launches of one kernel class:
+ *   UPIPE_KERNEL_ATTN_FWD  causal attention forward
+ *   UPIPE_KERNEL_ATTN_BWD  causal attention backward
+ *   UPIPE_KERNEL_GEMM      projection / gradient GEMMs
+ *   UPIPE_KERNEL_PREP      RoPE / layout / dO preparation passes
+ *   UPIPE_KERNEL_FINALIZE  dQ finalize, accumulator conversion, fills
+ * State is process-wide and not thread-safe.  Events are host-side HIP
+ * objects; no device memory is allocated.  Returns UPIPE_OK, UPIPE_EINVAL
+ * (bad kind or NULL output) or UPIPE_EHIP.
+ */
+#define UPIPE_KERNEL_ATTN_FWD 0
+#define UPIPE_KERNEL_ATTN_BWD 1
+#define UPIPE_KERNEL_GEMM 2
+#define UPIPE_KERNEL_PREP 3
+#define UPIPE_KERNEL_FINALIZE 4
+int upipe_profile_enable(int on);
+int upipe_profile_read(int kind, double* total_ms, int64_t* launches);
 
 /* Static, human-readable text for a status code.  Never NULL. */
 const char* upipe_strerror(int status);
