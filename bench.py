@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-CPU_SAMPLE_L = 2048
+CPU_SAMPLE_L = 8192
 
 KERNEL_SOURCES = {
     "attn_fwd": "headwise_chunked_context_amd/csrc/flash_fwd.hip",
@@ -86,7 +86,7 @@ def traffic_for(kind: str, workload: str):
 
 
 def cpu_baseline(w) -> dict:
-    """Time the fp64 oracle (as it stands) on the same layer shape at L=2048."""
+    """Time the fp64 oracle (as it stands) on the same layer shape at a short L."""
     import numpy as np  # noqa: F401
 
     import oracle

@@ -23,6 +23,14 @@ def from_dev_bf16(t):
     return synthetic.bf16_bits_to_f64(bits)
 
 
+def from_dev_bf16_f32(t):
+    """torch bfloat16 -> float32 numpy (exact; half the host memory of fp64)."""
+    import torch
+
+    bits = t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    return synthetic.bf16_bits_to_f32(bits)
+
+
 def from_dev_f32(t):
     return t.detach().cpu().numpy().astype(np.float64)
 
