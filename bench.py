@@ -43,7 +43,8 @@ CPU_SAMPLE_L = 8192
 
 KERNEL_SOURCES = {
     "attn_fwd": "headwise_chunked_context_amd/csrc/flash_fwd.hip",
-    "attn_bwd": "headwise_chunked_context_amd/csrc/flash_bwd.hip",
+    "attn_bwd_dkdv": "headwise_chunked_context_amd/csrc/flash_bwd.hip",
+    "attn_bwd_dq": "headwise_chunked_context_amd/csrc/flash_bwd.hip",
     "gemm": "headwise_chunked_context_amd/csrc/gemm.hip",
     "prep": "headwise_chunked_context_amd/csrc/prep.hip",
 }
@@ -202,14 +203,21 @@ def main() -> int:
     flops = model_flops(w)
     value = flops / (ms * 1e-3) / 1e12
 
-    # dominant kernel class and its roofline
+    # dominant kernel class and its roofline.  Algorithmic FLOPs per launch
+    # (one launch = one head chunk of hc query heads, P = L(L+1)/2 pairs):
+    #   attn_fwd       4 d P hc   (S = Q K^T and O = P V)
+    #   attn_bwd_dkdv  8 d P hc   (S, dP = dO V^T, dV = P^T dO, dK = dS^T Q)
+    #   attn_bwd_dq    2 d P hc   (dQ = dS K; its recomputed S and dP,
+    #                              4 d P hc more, are executed, not counted)
+    #   gemm           the projection GEMMs of a step / their launches
     d = w.head_dim
     P = w.L * (w.L + 1) / 2
     algo = {
-        "attn_fwd": 4.0 * d * P * hc,    # per launch (one chunk of hc heads)
-        "attn_bwd": 10.0 * d * P * hc,
+        "attn_fwd": 4.0 * d * P * hc,
+        "attn_bwd_dkdv": 8.0 * d * P * hc,
+        "attn_bwd_dq": 2.0 * d * P * hc,
     }
-    kinds = [k for k in ("attn_fwd", "attn_bwd", "gemm") if prof[k][1] > 0]
+    kinds = [k for k in ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm") if prof[k][1] > 0]
     dom = max(kinds, key=lambda k: prof[k][0])
     tot_ms, launches = prof[dom]
     avg_ms = tot_ms / launches
@@ -229,6 +237,14 @@ def main() -> int:
         "avg_launch_ms": round(avg_ms, 4),
         "launches": launches,
     }
+    # the whole attention backward (both kernels) against its 10 d P hc
+    nb = prof["attn_bwd_dkdv"][1]
+    if nb:
+        bwd_ms = (prof["attn_bwd_dkdv"][0] + prof["attn_bwd_dq"][0]) / nb
+        roofline["attn_bwd_tflops"] = round(10.0 * d * P * hc / (bwd_ms * 1e-3) / 1e12, 2)
+    nf = prof["attn_fwd"][1]
+    if nf:
+        roofline["attn_fwd_tflops"] = round(algo["attn_fwd"] / (prof["attn_fwd"][0] / nf * 1e-3) / 1e12, 2)
     breakdown = {k: {"ms_per_step": round(v[0] / args.steps, 3), "launches_per_step": v[1] // max(1, args.steps)}
                  for k, v in prof.items()}
 

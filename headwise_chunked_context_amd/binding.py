@@ -33,7 +33,8 @@ EXPORTS = (
     "upipe_version",
 )
 
-KERNEL_KINDS = {"attn_fwd": 0, "attn_bwd": 1, "gemm": 2, "prep": 3, "finalize": 4}
+KERNEL_KINDS = {"attn_fwd": 0, "attn_bwd_dkdv": 1, "attn_bwd_dq": 2, "gemm": 3, "prep": 4,
+                "finalize": 5}
 
 
 class UpipeError(RuntimeError):

@@ -77,11 +77,10 @@ int k_per_split(int64_t L, int splits) {
 // is affine in hc and independent of Hq.
 struct Plan {
   size_t staging;              // [L][(hc+2kc)d] bf16 GEMM output / gradient staging
-  size_t q_rm, q_t;            // [hc][Lp][d] bf16 (q_t bwd only)
-  size_t k_rm, k_t, v_rm, v_t; // [kc][Lp][d] / [kc][d][Lp] bf16
-  size_t do_rm, do_t;          // [hc][Lp][d] bf16 (bwd)
+  size_t q_rm;                 // [hc][Lp][d] bf16, rotated
+  size_t k_rm, v_rm;           // [kc][Lp][d] bf16 (k rotated; v fp16 in the forward)
+  size_t do_rm;                // [hc][Lp][d] bf16 (bwd)
   size_t lse2, dvec;           // [hc][Lp] fp32 (bwd)
-  size_t dq_acc;               // [hc][Lp][d] fp32 (bwd)
   size_t dk_acc, dv_acc;       // [kc][Lp][d] fp32 (bwd, only when a group spans chunks)
   size_t dw_acc;               // fp32 weight-gradient accumulator (bwd, projection mode)
   size_t total;
@@ -102,17 +101,12 @@ Plan make_plan(const Shape& s, int pass) {
   const size_t no = (size_t)-1;
   p.staging = s.proj ? take((size_t)s.L * width * 2) : no;
   p.q_rm = take(hc * head_bf16);
-  p.q_t = pass == UPIPE_PASS_BWD ? take(hc * head_bf16) : no;
   p.k_rm = take(kc * head_bf16);
-  p.k_t = pass == UPIPE_PASS_BWD ? take(kc * head_bf16) : no;
-  p.v_rm = pass == UPIPE_PASS_BWD ? take(kc * head_bf16) : no;
-  p.v_t = pass == UPIPE_PASS_FWD ? take(kc * head_bf16) : no;
+  p.v_rm = take(kc * head_bf16);
   if (pass == UPIPE_PASS_BWD) {
     p.do_rm = take(hc * head_bf16);
-    p.do_t = take(hc * head_bf16);
     p.lse2 = take(hc * Lp * 4);
     p.dvec = take(hc * Lp * 4);
-    p.dq_acc = take(hc * Lp * d * 4);
     // cross-chunk dK/dV accumulators (used while a KV group spans chunks;
     // always reserved so the size stays affine in the chunk)
     p.dk_acc = take(kc * Lp * d * 4);
@@ -121,7 +115,7 @@ Plan make_plan(const Shape& s, int pass) {
     // [D][hc d], dW_qkv[rows(c)] is [(hc+2kc) d][D]
     p.dw_acc = s.proj ? take(width * (size_t)s.D * 4) : no;
   } else {
-    p.do_rm = p.do_t = p.lse2 = p.dvec = p.dq_acc = p.dk_acc = p.dv_acc = p.dw_acc = no;
+    p.do_rm = p.lse2 = p.dvec = p.dk_acc = p.dv_acc = p.dw_acc = no;
   }
   p.total = off;
   return p;
@@ -159,7 +153,7 @@ int check_common(const Shape& s, double theta, const void* x, const void* w_qkv,
   } while (0)
 
 // ---- optional per-kernel-class timing (see upipe_profile_enable)
-constexpr int kKinds = 5;
+constexpr int kKinds = 6;
 struct Profiler {
   bool on = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[kKinds];
@@ -318,7 +312,7 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   uint16_t* staging = at<uint16_t>(workspace, p.staging);
   uint16_t* q_rm = at<uint16_t>(workspace, p.q_rm);
   uint16_t* k_rm = at<uint16_t>(workspace, p.k_rm);
-  uint16_t* v_t = at<uint16_t>(workspace, p.v_t);
+  uint16_t* v_rm = at<uint16_t>(workspace, p.v_rm);
   const int64_t qkv_ld = (int64_t)(s.Hq + 2 * s.Hkv) * d;
   const int width = (s.hc + 2 * s.kc) * d;
 
@@ -344,7 +338,7 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pa.nkv = ch.kv_first ? s.kc : 0;
     pa.q_rm = q_rm;
     pa.k_rm = k_rm;
-    pa.v_t = v_t;
+    pa.v_rm = v_rm;
     pa.L = s.L;
     pa.Lp = s.Lp;
     pa.rotate = s.proj ? 0 : 1;
@@ -356,7 +350,7 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     FwdArgs fa;
     fa.q = q_rm;
     fa.k = k_rm;
-    fa.vt = v_t;
+    fa.v = v_rm;
     fa.nh = s.hc;
     fa.group = s.G;
     fa.q_head0 = ch.h0;
@@ -416,21 +410,17 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   const int width = (s.hc + 2 * s.kc) * d;
   uint16_t* staging = at<uint16_t>(workspace, p.staging);
   uint16_t* q_rm = at<uint16_t>(workspace, p.q_rm);
-  uint16_t* q_t = at<uint16_t>(workspace, p.q_t);
   uint16_t* k_rm = at<uint16_t>(workspace, p.k_rm);
-  uint16_t* k_t = at<uint16_t>(workspace, p.k_t);
   uint16_t* v_rm = at<uint16_t>(workspace, p.v_rm);
   uint16_t* do_rm = at<uint16_t>(workspace, p.do_rm);
-  uint16_t* do_t = at<uint16_t>(workspace, p.do_t);
   float* lse2 = at<float>(workspace, p.lse2);
   float* dvec = at<float>(workspace, p.dvec);
-  float* dq_acc = at<float>(workspace, p.dq_acc);
   float* dk_acc = at<float>(workspace, p.dk_acc);
   float* dv_acc = at<float>(workspace, p.dv_acc);
   float* dw_acc = at<float>(workspace, p.dw_acc);
 
-  // accumulators start at zero; each finalize pass clears what it consumed
-  UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_zero(dq_acc, (size_t)s.hc * s.Lp * d * 4, st));
+  // the weight-gradient accumulator starts at zero; each conversion pass
+  // clears what it consumed
   if (dw_acc) UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_zero(dw_acc, (size_t)width * s.D * 4, st));
 
   for (int c = 0; c < s.Hq / s.hc; ++c) {
@@ -454,9 +444,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pa.nq = s.hc;
     pa.nkv = ch.kv_first ? s.kc : 0;
     pa.q_rm = q_rm;
-    pa.q_t = q_t;
     pa.k_rm = k_rm;
-    pa.k_t = k_t;
     pa.v_rm = v_rm;
     pa.L = s.L;
     pa.Lp = s.Lp;
@@ -472,7 +460,6 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pd.lse = lse + (int64_t)ch.h0 * s.L;
     pd.nh = s.hc;
     pd.do_rm = do_rm;
-    pd.do_t = do_t;
     pd.lse2 = lse2;
     pd.dvec = dvec;
     pd.L = s.L;
@@ -518,36 +505,31 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     }
     UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_dout(pd, st));
 
-    // 3. attention backward: dQ into the fp32 accumulator, dK/dV of the groups
+    // 3. attention backward: dK/dV of the chunk's KV groups, dQ of its heads
     BwdArgs ba;
     ba.q = q_rm;
-    ba.qt = q_t;
     ba.k = k_rm;
-    ba.kt = k_t;
     ba.v = v_rm;
     ba.dO = do_rm;
-    ba.dOt = do_t;
     ba.lse2 = lse2;
     ba.dvec = dvec;
-    ba.dq_acc = dq_acc;
     ba.dk_acc = dk_acc;
     ba.dv_acc = dv_acc;
     ba.kv_first = ch.kv_first ? 1 : 0;
     ba.kv_last = ch.kv_last ? 1 : 0;
-    uint16_t* grad_base;   // rows of [dq | dk | dv] for this chunk
-    int64_t grad_ld;
-    if (s.proj) {
-      grad_base = staging;
-      grad_ld = width;
+    if (s.proj) {   // rows of [dq | dk | dv] for this chunk, in the staging buffer
+      ba.dq_out = staging;
+      ba.dq_ld = width;
       ba.dk_out = staging + s.hc * d;
       ba.dv_out = staging + (s.hc + s.kc) * d;
-    } else {
-      grad_base = dx + (int64_t)ch.h0 * d;
-      grad_ld = qkv_ld;
+      ba.out_ld = width;
+    } else {        // straight into the caller's dqkv
+      ba.dq_out = dx + (int64_t)ch.h0 * d;
+      ba.dq_ld = qkv_ld;
       ba.dk_out = dx + (int64_t)(s.Hq + ch.g0) * d;
       ba.dv_out = dx + (int64_t)(s.Hq + s.Hkv + ch.g0) * d;
+      ba.out_ld = qkv_ld;
     }
-    ba.out_ld = s.proj ? width : qkv_ld;
     ba.nh = s.hc;
     ba.nkv = s.kc;
     ba.group = s.G;
@@ -558,8 +540,8 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     ba.scale_log2 = kLog2e / sqrtf((float)d);
     ba.scale = 1.f / sqrtf((float)d);
     ba.rope = rope;
-    UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_BWD, launch_flash_bwd(ba, st));
-    UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_dq_finalize(dq_acc, s.hc, s.L, s.Lp, ba.scale, grad_base, grad_ld, rope, st));
+    UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_BWD_DKDV, launch_flash_bwd_dkdv(ba, st));
+    UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_BWD_DQ, launch_flash_bwd_dq(ba, st));
 
     // 4. dx (+)= [dq | dk | dv] W_qkv[rows], dW_qkv[rows] = [dq | dk | dv]^T x
     if (s.proj) {

@@ -48,6 +48,70 @@ __device__ __forceinline__ f32x16 mfma32_f16(const u32x4& a, const u32x4& b, con
 // Row of the 32x32 accumulator element held in register r by a lane of half g.
 __device__ __forceinline__ int acc_row(int r, int g) { return (r >> 2) * 8 + g * 4 + (r & 3); }
 
+// ---------------------------------------------------------------- LDS tiles
+// Row-major tiles of 128 16-bit elements per row (256 B, no padding).  The
+// 16-byte chunk c of row r is stored at chunk position c ^ swz(r), where
+// swz swaps the two 2-bit halves of r % 16.  With it both access patterns
+// the kernels use are free of bank conflicts:
+//  * row-per-lane 16-byte reads (lane i of 16 reads row r0+i, one chunk):
+//    swz is a bijection on 16 consecutive rows;
+//  * transposed 8-byte reads (ds_read_b64_tr_b16, 4 rows x 32 bytes per
+//    16-lane group): rows r..r+3 (r % 4 == 0) land in four different
+//    64-byte quarters of the bank space.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int tile_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 3); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the 8-byte pieces addressed by lanes i/4, i/4+4, i/4+8, i/4+12.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// A-operand of a 32x32x16 MFMA whose m index runs along a row-major tile's
+// columns and whose k index runs down its rows (a transposed operand): lane
+// l gets column m0 + l % 32 and rows {k0 + 4g + j, k0 + 8 + 4g + j}, j < 4,
+// g = l / 32 -- the k order of the 32x32 accumulator layout, so the matching
+// B operand can come straight from accumulator registers.
+__device__ __forceinline__ u32x4 tile_read_t(const uint16_t* tile, int k0, int m0, int lane) {
+  const int s = lane & 15, grp2 = (lane >> 4) & 1, g = lane >> 5;
+  const int col = m0 + 16 * grp2 + 4 * (s & 3);
+  const int chunk = col >> 3, half = (col & 7);
+  const int r0 = k0 + 4 * g + (s >> 2);
+  u32x2 lo = lds_read_tr16(tile + tile_off(r0, chunk) + half);
+  u32x2 hi = lds_read_tr16(tile + tile_off(r0 + 8, chunk) + half);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Row-per-lane operand: row r, eight elements starting at column 8*chunk.
+__device__ __forceinline__ u32x4 tile_read_row(const uint16_t* tile, int row, int chunk) {
+  return *reinterpret_cast<const u32x4*>(tile + tile_off(row, chunk));
+}
+
+// Cooperative global -> LDS copy of `rows` x 128 elements (rows * 16 chunks),
+// 256 threads, into the swizzled layout; src rows are 128 elements apart.
+template <int ROWS>
+struct TileCopy {
+  static constexpr int N = ROWS * 16 / 256;
+  u32x4 v[N];
+  __device__ __forceinline__ void load(const uint16_t* src, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int c = tid + 256 * i;
+      v[i] = *reinterpret_cast<const u32x4*>(src + (c >> 4) * 128 + (c & 15) * 8);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int c = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(tile + tile_off(c >> 4, c & 15)) = v[i];
+    }
+  }
+};
+
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};

@@ -3,47 +3,49 @@
 // Chain rule of exact softmax attention (FlashAttention, Builds-on list of
 // "Untied Ulysses: Memory-Efficient Context Parallelism via Headwise
 // Chunking"): with P recomputed from the saved log-sum-exp,
-//   dV += P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = dS K / sqrt(d),
-//   dK += dS^T Q / sqrt(d),     D_i = dO_i . O_i.
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = dS K / sqrt(d),
+//   dK = dS^T Q / sqrt(d),      D_i = dO_i . O_i.
 //
-// Layout choices for CDNA4:
-//  * a workgroup owns 128 keys of one KV head (4 waves x 32 keys) and walks
-//    every q head of that KV group inside the chunk and every 64-query tile
-//    at or below the diagonal, so dK/dV of the group accumulate in registers
-//    (fp32) across the group's heads with no atomics;
-//  * scores are computed S = Q K^T so each lane owns ONE key: the S/dP
-//    accumulators feed dV^T = dO^T P and dK^T = Q^T dS as MFMA B operands
-//    straight from registers, with dO^T/Q^T read from d-major copies;
-//  * dQ = dS K is a cross-wave contraction over the workgroup's 128 keys:
-//    dS goes through LDS once and each wave adds a 64x32 slab of dQ into an
-//    fp32 accumulator with hardware float atomics;
-//  * at the last chunk of a KV group the epilogue scales dK, applies the
-//    inverse RoPE in registers and writes bf16; when a group spans several
-//    chunks the partial dK/dV live in fp32 workspace between chunks.
+// Two kernels, so that no gradient needs atomics:
+//  * dkdv: a workgroup owns 128 keys of one KV head (4 waves x 32 keys) and
+//    walks every q head of that KV group in the chunk and every 64-query tile
+//    at or below the diagonal, accumulating dK/dV of the group in fp32
+//    registers.  Scores are computed S = Q K^T so each lane owns ONE key:
+//    the S/dP accumulators feed dV^T = dO^T P and dK^T = Q^T dS as MFMA B
+//    operands straight from registers, with the dO^T / Q^T operands read
+//    from the row-major tiles by the LDS transpose read.  Query tiles are
+//    walked from the END of the sequence towards
+//    the diagonal, so workgroups that start together stream the same Q/dO
+//    tiles and share them in L2.  The next tile's loads are issued before the
+//    current tile's MFMAs.
+//  * dq: a workgroup owns 128 queries of one q head (4 waves x 32 queries)
+//    and walks the key tiles up to the diagonal like the forward kernel:
+//    S^T = K Q^T and dP^T = V dO^T give each lane ONE query (its LSE and D
+//    are per-lane scalars), dS^T feeds dQ^T = K^T dS^T as a B operand from
+//    registers and K^T is the transpose read of the same K tile.  The
+//    epilogue scales dQ, applies the inverse RoPE in registers and writes
+//    bf16.
+// All tiles are [rows][128] in the XOR-swizzled layout of common.h.
+// dQ costs a second evaluation of S and dP (+4 d flops per score pair over
+// the 10 of one fused kernel) in exchange for no fp32 read-modify-write
+// traffic to memory.
 #include "kernels.h"
 
 namespace upipe {
 namespace {
 
-constexpr int BNK = 128;       // keys per workgroup
-constexpr int BMQ = 64;        // queries per step
-constexpr int RP = 128 + 8;    // row-major [*, 128] tile pitch (bf16)
-constexpr int TP = BMQ + 8;    // d-major [128][64] tile pitch (bf16)
-constexpr int SP = BNK + 8;    // dS [64][128] pitch (bf16)
+constexpr int BNK = 128;       // keys per dkdv workgroup
+constexpr int BMQ = 64;        // queries per dkdv step
 
-struct __attribute__((aligned(16))) BwdSmem {
-  uint16_t Q[BMQ * RP];
-  uint16_t dO[BMQ * RP];
-  uint16_t QT[128 * TP];
-  uint16_t dOT[128 * TP];
-  uint16_t dS[BMQ * SP];
-  uint16_t KT[128 * SP];
+struct __attribute__((aligned(16))) DkdvSmem {
+  uint16_t Q[BMQ * 128];
+  uint16_t dO[BMQ * 128];
   float lse2[BMQ];
   float dvec[BMQ];
 };
 
-__global__ __launch_bounds__(256) void flash_bwd_kernel(BwdArgs a) {
-  __shared__ BwdSmem sm;
+__global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ DkdvSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -57,7 +59,6 @@ __global__ __launch_bounds__(256) void flash_bwd_kernel(BwdArgs a) {
 
   const uint16_t* kp = a.k + (int64_t)kv * a.Lp * 128;
   const uint16_t* vp = a.v + (int64_t)kv * a.Lp * 128;
-  const uint16_t* ktp = a.kt + (int64_t)kv * a.Lp * 128;
 
   // K and V of this lane's key as B operands (column = key, k = d)
   u32x4 kreg[8], vreg[8];
@@ -65,14 +66,6 @@ __global__ __launch_bounds__(256) void flash_bwd_kernel(BwdArgs a) {
   for (int ks = 0; ks < 8; ++ks) {
     kreg[ks] = *reinterpret_cast<const u32x4*>(kp + my_key * 128 + ks * 16 + g * 8);
     vreg[ks] = *reinterpret_cast<const u32x4*>(vp + my_key * 128 + ks * 16 + g * 8);
-  }
-  // K^T of the workgroup's 128 keys for the dQ contraction
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int c = tid + 256 * i;
-    int dd = c >> 4, cc = c & 15;
-    *reinterpret_cast<u32x4*>(&sm.KT[dd * SP + cc * 8]) =
-        *reinterpret_cast<const u32x4*>(ktp + (int64_t)dd * a.Lp + k0 + cc * 8);
   }
 
   f32x16 acc_dk[4], acc_dv[4];
@@ -88,131 +81,99 @@ __global__ __launch_bounds__(256) void flash_bwd_kernel(BwdArgs a) {
   int j1 = j0 + a.group;
   if (j0 < 0) j0 = 0;
   if (j1 > a.nh) j1 = a.nh;
-  const int qs0 = (int)(k0 / BMQ);
-  const int qs1 = (int)((a.L + BMQ - 1) / BMQ);
+  const int qs_lo = (int)(k0 / BMQ);                 // first tile that sees these keys
+  const int qs_hi = (int)((a.L + BMQ - 1) / BMQ);    // one past the last tile
+  const int steps_per_head = qs_hi - qs_lo;
+  const int nsteps = steps_per_head * (j1 - j0);
 
-  for (int j = j0; j < j1; ++j) {
-    const uint16_t* qp = a.q + (int64_t)j * a.Lp * 128;
-    const uint16_t* qtp = a.qt + (int64_t)j * a.Lp * 128;
-    const uint16_t* dop = a.dO + (int64_t)j * a.Lp * 128;
-    const uint16_t* dotp = a.dOt + (int64_t)j * a.Lp * 128;
-    const float* lsep = a.lse2 + (int64_t)j * a.Lp;
-    const float* dvp = a.dvec + (int64_t)j * a.Lp;
-    float* dqp = a.dq_acc + (int64_t)j * a.Lp * 128;
+  // step s -> (head j, query tile qs), tiles walked from the end backwards
+  auto step_head = [&](int s) { return j0 + s / steps_per_head; };
+  auto step_tile = [&](int s) { return qs_hi - 1 - s % steps_per_head; };
 
-    for (int qs = qs0; qs < qs1; ++qs) {
-      const int64_t q0 = (int64_t)qs * BMQ;
-      __syncthreads();  // previous step's LDS reads are done
+  TileCopy<BMQ> pq, pdo;
+  float plse = 0.f;
+  auto load_step = [&](int s) {
+    const int j = step_head(s);
+    const int64_t q0 = (int64_t)step_tile(s) * BMQ;
+    pq.load(a.q + ((int64_t)j * a.Lp + q0) * 128, tid);
+    pdo.load(a.dO + ((int64_t)j * a.Lp + q0) * 128, tid);
+    if (tid < BMQ) plse = a.lse2[(int64_t)j * a.Lp + q0 + tid];
+    else if (tid < 2 * BMQ) plse = a.dvec[(int64_t)j * a.Lp + q0 + tid - BMQ];
+  };
+  auto store_step = [&]() {
+    pq.store(sm.Q, tid);
+    pdo.store(sm.dO, tid);
+    if (tid < BMQ) sm.lse2[tid] = plse;
+    else if (tid < 2 * BMQ) sm.dvec[tid - BMQ] = plse;
+  };
+
+  if (nsteps > 0) load_step(0);
+  for (int s = 0; s < nsteps; ++s) {
+    const int64_t q0 = (int64_t)step_tile(s) * BMQ;
+    __syncthreads();  // previous step's LDS reads are done
+    store_step();
+    __syncthreads();
+    if (s + 1 < nsteps) load_step(s + 1);  // in flight during this step's MFMAs
+
+    const bool need_mask = (q0 < k0 + BNK) || (q0 + BMQ > a.L);
+    // S = Q K^T and dP = dO V^T: element (query qb*32+acc_row(r,g), key my_key)
+    f32x16 sv[2], dp[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int c2 = tid + 256 * i;
-        int row = c2 >> 4, cc = c2 & 15;
-        *reinterpret_cast<u32x4*>(&sm.Q[row * RP + cc * 8]) =
-            *reinterpret_cast<const u32x4*>(qp + (q0 + row) * 128 + cc * 8);
-        *reinterpret_cast<u32x4*>(&sm.dO[row * RP + cc * 8]) =
-            *reinterpret_cast<const u32x4*>(dop + (q0 + row) * 128 + cc * 8);
-        int dd = c2 >> 3, tc = c2 & 7;
-        *reinterpret_cast<u32x4*>(&sm.QT[dd * TP + tc * 8]) =
-            *reinterpret_cast<const u32x4*>(qtp + (int64_t)dd * a.Lp + q0 + tc * 8);
-        *reinterpret_cast<u32x4*>(&sm.dOT[dd * TP + tc * 8]) =
-            *reinterpret_cast<const u32x4*>(dotp + (int64_t)dd * a.Lp + q0 + tc * 8);
+    for (int qb = 0; qb < 2; ++qb) {
+      sv[qb] = f32x16{};
+      dp[qb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        sv[qb] = mfma32(tile_read_row(sm.Q, qb * 32 + l32, 2 * ks + g), kreg[ks], sv[qb]);
+        dp[qb] = mfma32(tile_read_row(sm.dO, qb * 32 + l32, 2 * ks + g), vreg[ks], dp[qb]);
       }
-      if (tid < BMQ) sm.lse2[tid] = lsep[q0 + tid];
-      else if (tid < 2 * BMQ) sm.dvec[tid - BMQ] = dvp[q0 + tid - BMQ];
-      __syncthreads();
-
-      const bool need_mask = (q0 < k0 + BNK) || (q0 + BMQ > a.L);
-      // S = Q K^T and dP = dO V^T: element (query qb*32+acc_row(r,g), key my_key)
-      f32x16 s[2], dp[2];
+    }
+    u32x4 pP[4], pS[4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
-        const uint16_t* qb_base = &sm.Q[(qb * 32 + l32) * RP + g * 8];
-        const uint16_t* db_base = &sm.dO[(qb * 32 + l32) * RP + g * 8];
+    for (int qb = 0; qb < 2; ++qb) {
+      float pv[16], dsv[16];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          s[qb] = mfma32(*reinterpret_cast<const u32x4*>(qb_base + ks * 16), kreg[ks], s[qb]);
-          dp[qb] = mfma32(*reinterpret_cast<const u32x4*>(db_base + ks * 16), vreg[ks], dp[qb]);
-        }
-      }
-      u32x4 pP[4], pS[4];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int qi = qb * 32 + r4 * 8 + g * 4;
+        f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[qi]);
+        f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dvec[qi]);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float pv[16], dsv[16];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int qi = qb * 32 + r4 * 8 + g * 4;
-          f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[qi]);
-          f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dvec[qi]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = r4 * 4 + i;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -l4[i]));
-            if (need_mask) {
-              const int64_t qrow = q0 + qi + i;
-              if (my_key > qrow || qrow >= a.L) p = 0.f;
-            }
-            pv[r] = p;
-            dsv[r] = p * (dp[qb][r] - d4[i]);
+        for (int i = 0; i < 4; ++i) {
+          const int r = r4 * 4 + i;
+          float p = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], c, -l4[i]));
+          if (need_mask) {
+            const int64_t qrow = q0 + qi + i;
+            if (my_key > qrow || qrow >= a.L) p = 0.f;
           }
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            pP[qb * 2 + h][t] = pack_bf16x2(pv[8 * h + 2 * t], pv[8 * h + 2 * t + 1]);
-            pS[qb * 2 + h][t] = pack_bf16x2(dsv[8 * h + 2 * t], dsv[8 * h + 2 * t + 1]);
-          }
-        }
-        // dS to LDS, query-major with keys contiguous, for the dQ contraction
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          uint32_t w = pS[qb * 2 + (r >> 3)][(r & 7) >> 1];
-          uint16_t hbits = (r & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
-          sm.dS[(qb * 32 + acc_row(r, g)) * SP + 32 * wave + l32] = hbits;
+          pv[r] = p;
+          dsv[r] = p * (dp[qb][r] - d4[i]);
         }
       }
-      // dV^T += dO^T P, dK^T += Q^T dS; B slot t of step st is query
-      // 16*st + 8*(t/4) + 4*g + t%4
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const uint16_t* ob = &sm.dOT[(db * 32 + l32) * TP + st * 16 + g * 4];
-          const uint16_t* qtb = &sm.QT[(db * 32 + l32) * TP + st * 16 + g * 4];
-          u32x2 olo = *reinterpret_cast<const u32x2*>(ob);
-          u32x2 ohi = *reinterpret_cast<const u32x2*>(ob + 8);
-          u32x2 qlo = *reinterpret_cast<const u32x2*>(qtb);
-          u32x2 qhi = *reinterpret_cast<const u32x2*>(qtb + 8);
-          acc_dv[db] = mfma32(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pP[st], acc_dv[db]);
-          acc_dk[db] = mfma32(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, pS[st], acc_dk[db]);
+        for (int t = 0; t < 4; ++t) {
+          pP[qb * 2 + h][t] = pack_bf16x2(pv[8 * h + 2 * t], pv[8 * h + 2 * t + 1]);
+          pS[qb * 2 + h][t] = pack_bf16x2(dsv[8 * h + 2 * t], dsv[8 * h + 2 * t + 1]);
         }
       }
-      __syncthreads();  // dS complete
-      // dQ[:, 32*wave .. +32] += dS (64 x 128 keys) K (128 keys x 32 d)
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS; B slot t of step st is query
+    // 16*st + 8*(t/4) + 4*g + t%4
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 dq = f32x16{};
-        const uint16_t* sb = &sm.dS[(qb * 32 + l32) * SP + g * 8];
-        const uint16_t* kb = &sm.KT[(32 * wave + l32) * SP + g * 8];
+    for (int st = 0; st < 4; ++st) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          dq = mfma32(*reinterpret_cast<const u32x4*>(sb + ks * 16),
-                      *reinterpret_cast<const u32x4*>(kb + ks * 16), dq);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t qrow = q0 + qb * 32 + acc_row(r, g);
-          atomicAdd(dqp + qrow * 128 + 32 * wave + l32, dq[r]);
-        }
+      for (int db = 0; db < 4; ++db) {
+        acc_dv[db] = mfma32(tile_read_t(sm.dO, st * 16, db * 32, lane), pP[st], acc_dv[db]);
+        acc_dk[db] = mfma32(tile_read_t(sm.Q, st * 16, db * 32, lane), pS[st], acc_dk[db]);
       }
     }
   }
 
   // ---- epilogue: element (d = db*32 + acc_row(r,g), key my_key)
   if (my_key >= a.L) return;
-  float* dka = a.dk_acc ? a.dk_acc + ((int64_t)kv * a.Lp + my_key) * 128 : nullptr;
-  float* dva = a.dv_acc ? a.dv_acc + ((int64_t)kv * a.Lp + my_key) * 128 : nullptr;
+  float* dka = a.dk_acc + ((int64_t)kv * a.Lp + my_key) * 128;
+  float* dva = a.dv_acc + ((int64_t)kv * a.Lp + my_key) * 128;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -250,11 +211,146 @@ __global__ __launch_bounds__(256) void flash_bwd_kernel(BwdArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ dQ
+constexpr int QBM = 128;       // queries per dq workgroup
+constexpr int QBN = 64;        // keys per dq step
+
+struct __attribute__((aligned(16))) DqSmem {
+  uint16_t K[2][QBN * 128];
+  uint16_t V[2][QBN * 128];
+};
+
+__global__ __launch_bounds__(256) void flash_bwd_dq_kernel(BwdArgs a) {
+  __shared__ DqSmem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+
+  const int nqt = (int)(a.Lp / QBM);
+  const int head = blockIdx.x % a.nh;
+  const int qt = nqt - 1 - (int)(blockIdx.x / a.nh);
+  const int64_t q0 = (int64_t)qt * QBM;
+  if (q0 >= a.L) return;
+  const int kvh = (a.q_head0 + head) / a.group - a.kv_head0;
+  const uint16_t* qp = a.q + (int64_t)head * a.Lp * 128;
+  const uint16_t* dop = a.dO + (int64_t)head * a.Lp * 128;
+  const uint16_t* kp = a.k + (int64_t)kvh * a.Lp * 128;
+  const uint16_t* vp = a.v + (int64_t)kvh * a.Lp * 128;
+
+  const int64_t r0 = q0 + 32 * wave;
+  const int64_t my_q = r0 + l32;
+
+  // Q and dO of this lane's query as B operands (column = query, k = d)
+  u32x4 qreg[8], doreg[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qreg[ks] = *reinterpret_cast<const u32x4*>(qp + my_q * 128 + ks * 16 + g * 8);
+    doreg[ks] = *reinterpret_cast<const u32x4*>(dop + my_q * 128 + ks * 16 + g * 8);
+  }
+  const float lse2 = a.lse2[(int64_t)head * a.Lp + my_q];
+  const float dval = a.dvec[(int64_t)head * a.Lp + my_q];
+
+  const int64_t kv_end = (q0 + QBM < a.L) ? q0 + QBM : a.L;
+  const int n_kt = (int)((kv_end + QBN - 1) / QBN);
+
+  TileCopy<QBN> pk, pv;
+  auto load_kv = [&](int kt) {
+    const int64_t kk0 = (int64_t)kt * QBN;
+    pk.load(kp + kk0 * 128, tid);
+    pv.load(vp + kk0 * 128, tid);
+  };
+  auto store_kv = [&](int buf) {
+    pk.store(sm.K[buf], tid);
+    pv.store(sm.V[buf], tid);
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  const float c = a.scale_log2;
+
+  load_kv(0);
+  store_kv(0);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < n_kt) load_kv(kt + 1);
+    const int64_t kstart = (int64_t)kt * QBN;
+    if (kstart <= r0 + 31) {
+      const bool need_mask = kstart + QBN - 1 > r0;
+      // S^T = K Q^T, dP^T = V dO^T: element (key kb*32+acc_row(r,g), query my_q)
+      f32x16 sv[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sv[kb] = f32x16{};
+        dp[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          sv[kb] = mfma32(tile_read_row(sm.K[cur], kb * 32 + l32, 2 * ks + g), qreg[ks], sv[kb]);
+          dp[kb] = mfma32(tile_read_row(sm.V[cur], kb * 32 + l32, 2 * ks + g), doreg[ks], dp[kb]);
+        }
+      }
+      u32x4 pS[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], c, -lse2));
+          if (need_mask && kstart + kb * 32 + acc_row(r, g) > my_q) p = 0.f;
+          ds[r] = p * (dp[kb][r] - dval);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            pS[kb * 2 + h][t] = pack_bf16x2(ds[8 * h + 2 * t], ds[8 * h + 2 * t + 1]);
+      }
+      // dQ^T += K^T dS^T; B slot t of step st is key 16*st + 8*(t/4) + 4*g + t%4
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          acc[db] = mfma32(tile_read_t(sm.K[cur], st * 16, db * 32, lane), pS[st], acc[db]);
+      }
+    }
+    if (kt + 1 < n_kt) store_kv(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (my_q >= a.L) return;
+  // element (d = db*32 + acc_row(r,g), query my_q): scale, inverse RoPE, bf16
+  uint16_t* orow = a.dq_out + my_q * a.dq_ld + (int64_t)head * 128;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int d = db * 32 + j4 * 8 + g * 4;
+      float r4[4];
+#pragma unroll
+      for (int pi = 0; pi < 2; ++pi) {
+        float cs, sn;
+        rope_cos_sin(a.rope, my_q, (d >> 1) + pi, cs, sn);
+        float e = acc[db][4 * j4 + 2 * pi] * a.scale, o = acc[db][4 * j4 + 2 * pi + 1] * a.scale;
+        r4[2 * pi] = e * cs + o * sn;
+        r4[2 * pi + 1] = -e * sn + o * cs;
+      }
+      u32x2 w = {pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
+      *reinterpret_cast<u32x2*>(orow + d) = w;
+    }
+}
+
 }  // namespace
 
-hipError_t launch_flash_bwd(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_flash_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.Lp / BNK) * a.nkv));
-  hipLaunchKernelGGL(flash_bwd_kernel, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(flash_bwd_dkdv_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flash_bwd_dq(const BwdArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.Lp / QBM) * a.nh));
+  hipLaunchKernelGGL(flash_bwd_dq_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -15,8 +15,11 @@
 //    a 32-key block, so the row max/sum need one cross-half exchange
 //    (lane ^ 32) and the output rescale is a per-lane scalar;
 //  * the P^T accumulator registers feed the O^T = V^T P^T MFMA directly as
-//    its B operand (no LDS round trip); V^T comes from a d-major copy so the
-//    A operand reads are two 8-byte runs of keys;
+//    its B operand (no LDS round trip); the V^T operand is read from the
+//    row-major V tile with the LDS transpose read (ds_read_b64_tr_b16), in
+//    the key order of the accumulator layout;
+//  * K and V tiles use the XOR-swizzled 256-byte-row layout (no padding, no
+//    bank conflicts for either read pattern);
 //  * P and V enter O = P V as fp16 (v_mfma_f32_32x32x16_f16, same rate as
 //    bf16): P lies in [0, 1] and fp16's 10-bit mantissa keeps the forward
 //    output inside its error budget where bf16's 7 bits do not;
@@ -31,12 +34,10 @@ namespace {
 
 constexpr int BM = 128;       // queries per workgroup
 constexpr int BN = 64;        // keys per step
-constexpr int KP = 128 + 8;   // K tile pitch (bf16)
-constexpr int VP = BN + 8;    // V^T tile pitch (bf16)
 
 __global__ __launch_bounds__(256) void flash_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][128 * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * 128];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FwdArgs a) {
   const int kvh = (a.q_head0 + head) / a.group - a.kv_head0;
   const uint16_t* qp = a.q + (int64_t)head * a.Lp * 128;
   const uint16_t* kp = a.k + (int64_t)kvh * a.Lp * 128;
-  const uint16_t* vtp = a.vt + (int64_t)kvh * a.Lp * 128;
+  const uint16_t* vp = a.v + (int64_t)kvh * a.Lp * 128;
 
   const int64_t r0 = q0 + 32 * wave;  // first query row of this wave
   const int64_t my_q = r0 + l32;
@@ -64,27 +65,15 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FwdArgs a) {
   const int64_t kv_end = (q0 + BM < a.L) ? q0 + BM : a.L;
   const int n_kt = (int)((kv_end + BN - 1) / BN);
 
-  u32x4 pk[4], pv[4];
+  TileCopy<BN> pk, pv;
   auto load_kv = [&](int kt) {
     const int64_t k0 = (int64_t)kt * BN;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + 256 * i;
-      int row = c >> 4, cc = c & 15;
-      pk[i] = *reinterpret_cast<const u32x4*>(kp + (k0 + row) * 128 + cc * 8);
-      int dd = c >> 3, vc = c & 7;
-      pv[i] = *reinterpret_cast<const u32x4*>(vtp + (int64_t)dd * a.Lp + k0 + vc * 8);
-    }
+    pk.load(kp + k0 * 128, tid);
+    pv.load(vp + k0 * 128, tid);
   };
   auto store_kv = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + 256 * i;
-      int row = c >> 4, cc = c & 15;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * KP + cc * 8]) = pk[i];
-      int dd = c >> 3, vc = c & 7;
-      *reinterpret_cast<u32x4*>(&Vs[buf][dd * VP + vc * 8]) = pv[i];
-    }
+    pk.store(Ks[buf], tid);
+    pv.store(Vs[buf], tid);
   };
 
   f32x16 acc_o[4];
@@ -108,12 +97,9 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = f32x16{};
-        const uint16_t* kbase = &Ks[cur][(kb * 32 + l32) * KP + g * 8];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          u32x4 av = *reinterpret_cast<const u32x4*>(kbase + ks * 16);
-          s[kb] = mfma32(av, qreg[ks], s[kb]);
-        }
+        for (int ks = 0; ks < 8; ++ks)
+          s[kb] = mfma32(tile_read_row(Ks[cur], kb * 32 + l32, 2 * ks + g), qreg[ks], s[kb]);
       }
       if (need_mask) {
 #pragma unroll
@@ -159,13 +145,8 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const uint16_t* vb = &Vs[cur][(db * 32 + l32) * VP + st * 16 + g * 4];
-          u32x2 lo = *reinterpret_cast<const u32x2*>(vb);
-          u32x2 hi = *reinterpret_cast<const u32x2*>(vb + 8);
-          u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          acc_o[db] = mfma32_f16(av, pb[st], acc_o[db]);
-        }
+        for (int db = 0; db < 4; ++db)
+          acc_o[db] = mfma32_f16(tile_read_t(Vs[cur], st * 16, db * 32, lane), pb[st], acc_o[db]);
       }
     }
     if (kt + 1 < n_kt) store_kv(cur ^ 1);

@@ -52,30 +52,28 @@ hipError_t launch_acc_to_bf16(float* acc, int M, int N, uint16_t* dst, int64_t l
                               const RowSegments& rows, hipStream_t s);
 
 // ---------------------------------------------------------------- prep
-// Copies heads into the attention kernels' head-major layout, padded with
-// zero rows to Lp, rotating q and k heads (RoPE) on the way unless the
-// source is already rotated (the projection GEMM rotates in its epilogue).
+// Copies a chunk's heads into the attention kernels' head-major layout
+// [head][Lp][128], padded with zero rows to Lp, rotating q and k heads (RoPE)
+// on the way unless the source is already rotated (the projection GEMM
+// rotates in its epilogue), and converting v between bf16 and fp16.
 struct PrepArgs {
   const uint16_t* src_q;   // head j of each kind starts at src + j*128; rows every src_ld
   const uint16_t* src_k;
   const uint16_t* src_v;
   int64_t src_ld;
   int nq, nkv;
-  uint16_t* q_rm;          // [nq][Lp][128]   (may be null)
-  uint16_t* q_t;           // [nq][128][Lp]   (may be null)
+  uint16_t* q_rm;          // [nq][Lp][128]
   uint16_t* k_rm;          // [nkv][Lp][128]
-  uint16_t* k_t;           // [nkv][128][Lp]
   uint16_t* v_rm;          // [nkv][Lp][128]
-  uint16_t* v_t;           // [nkv][128][Lp]
   int64_t L, Lp;
   int rotate;              // apply RoPE to q and k heads
   int v_src_f16;           // v source holds fp16 bits (else bf16)
-  int v_out_f16;           // write v_rm / v_t as fp16 (else bf16)
+  int v_out_f16;           // write v as fp16 (else bf16)
 };
 hipError_t launch_prep_qkv(const PrepArgs& a, const RopeTable& t, hipStream_t s);
 
-// dO prep for the backward: head-major dO and dO^T, D_i = dO_i . O_i and the
-// base-2 log-sum-exp of each row, all padded to Lp.
+// dO prep for the backward: head-major dO, D_i = dO_i . O_i and the base-2
+// log-sum-exp of each row, all padded to Lp.
 struct PrepDoutArgs {
   const uint16_t* src_do;  // head j at src_do + j*128, row stride do_ld
   int64_t do_ld;
@@ -84,17 +82,11 @@ struct PrepDoutArgs {
   const float* lse;        // head j at lse + j*L
   int nh;
   uint16_t* do_rm;         // [nh][Lp][128]
-  uint16_t* do_t;          // [nh][128][Lp]
   float* lse2;             // [nh][Lp]
   float* dvec;             // [nh][Lp]
   int64_t L, Lp;
 };
 hipError_t launch_prep_dout(const PrepDoutArgs& a, hipStream_t s);
-
-// dq_acc [nh][Lp][128] fp32 -> scale, inverse RoPE -> bf16 dst + row*ld + j*128;
-// clears dq_acc afterwards.
-hipError_t launch_dq_finalize(float* dq_acc, int nh, int64_t L, int64_t Lp, float scale,
-                              uint16_t* dst, int64_t ld, const RopeTable& t, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
@@ -102,7 +94,7 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 struct FwdArgs {
   const uint16_t* q;    // [nh][Lp][128], rotated
   const uint16_t* k;    // [nkv][Lp][128], rotated
-  const uint16_t* vt;   // [nkv][128][Lp] fp16
+  const uint16_t* v;    // [nkv][Lp][128] fp16
   int nh;               // query heads in this chunk
   int group;            // G = Hq / Hkv
   int q_head0;          // global index of the chunk's first q head
@@ -117,21 +109,18 @@ hipError_t launch_flash_fwd(const FwdArgs& a, hipStream_t s);
 
 struct BwdArgs {
   const uint16_t* q;     // [nh][Lp][128] rotated
-  const uint16_t* qt;    // [nh][128][Lp]
   const uint16_t* k;     // [nkv][Lp][128] rotated
-  const uint16_t* kt;    // [nkv][128][Lp]
   const uint16_t* v;     // [nkv][Lp][128]
   const uint16_t* dO;    // [nh][Lp][128]
-  const uint16_t* dOt;   // [nh][128][Lp]
   const float* lse2;     // [nh][Lp]
   const float* dvec;     // [nh][Lp]
-  float* dq_acc;         // [nh][Lp][128] fp32, atomically accumulated
-  float* dk_acc;         // [nkv][Lp][128] fp32 cross-chunk accumulators (null if unused)
+  float* dk_acc;         // [nkv][Lp][128] fp32 cross-chunk accumulators
   float* dv_acc;
   int kv_first, kv_last; // this chunk starts / finishes its KV groups
   uint16_t* dk_out;      // bf16 rows: dk of kv j at dk_out + row*out_ld + j*128 (when kv_last)
   uint16_t* dv_out;
-  int64_t out_ld;
+  uint16_t* dq_out;      // bf16 rows: dq of q head j at dq_out + row*dq_ld + j*128
+  int64_t out_ld, dq_ld;
   int nh, nkv;
   int group;             // G
   int q_head0, kv_head0; // global indices (q head h uses kv head h / G)
@@ -140,6 +129,9 @@ struct BwdArgs {
   float scale;           // 1/sqrt(d)
   RopeTable rope;
 };
-hipError_t launch_flash_bwd(const BwdArgs& a, hipStream_t s);
+// dK, dV of the chunk's KV heads (key-stationary) ...
+hipError_t launch_flash_bwd_dkdv(const BwdArgs& a, hipStream_t s);
+// ... and dQ of its q heads (query-stationary), written inverse-rotated in bf16
+hipError_t launch_flash_bwd_dq(const BwdArgs& a, hipStream_t s);
 
 }  // namespace upipe

@@ -1,61 +1,51 @@
 // Memory-bound passes around the attention kernels (gfx950):
 //   prep_qkv    head-major copies of a chunk's q/k/v, RoPE on q and k,
-//               optional transposed copies (d-major) for the MFMA operands
-//               that contract over the sequence, zero padding to Lp rows,
-//               v converted between bf16 and fp16 as the consumer needs;
+//               zero padding to Lp rows, v converted between bf16 and fp16
+//               as the consumer needs;
 //   prep_dout   the same for dO, plus D_i = dO_i . O_i and LSE in base 2;
-//   dq_finalize fp32 dQ accumulator -> scaled, inverse-rotated bf16;
 //   zero        fill kernel (used instead of hipMemsetAsync).
 // Each workgroup owns 64 rows x 128 columns of one head: coalesced 16-byte
-// row reads, a transpose through LDS, coalesced 128-byte column writes.
+// reads and writes along the rows.
 #include "kernels.h"
 
 namespace upipe {
 namespace {
 
 constexpr int ROWS = 64;
-constexpr int T_PITCH = ROWS + 8;  // bf16 pitch of the [128][64] transpose tile
 
 // rotate 8 consecutive elements (4 pairs starting at pair p0) of one row
-__device__ __forceinline__ u32x4 rotate8(u32x4 v, const RopeTable& t, int64_t pos, int p0,
-                                         bool inverse) {
+__device__ __forceinline__ u32x4 rotate8(u32x4 v, const RopeTable& t, int64_t pos, int p0) {
   u32x4 out;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float c, s;
     rope_cos_sin(t, pos, p0 + j, c, s);
-    if (inverse) s = -s;
     float e = bf16_lo(v[j]), o = bf16_hi(v[j]);
     out[j] = pack_bf16x2(e * c - o * s, e * s + o * c);
   }
   return out;
 }
 
+// one workgroup per 64 rows of one head slot (q heads, then k, then v)
 __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a, RopeTable t) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * T_PITCH];
   const int slot = blockIdx.y;
   const int64_t r0 = (int64_t)blockIdx.x * ROWS;
   const uint16_t* src;
-  uint16_t *rm, *tr;
-  bool rot;
-  const bool is_v = slot >= a.nq + a.nkv;
+  uint16_t* dst;
+  bool rot = a.rotate != 0, is_v = false;
   if (slot < a.nq) {
     src = a.src_q + slot * 128;
-    rm = a.q_rm ? a.q_rm + (int64_t)slot * a.Lp * 128 : nullptr;
-    tr = a.q_t ? a.q_t + (int64_t)slot * a.Lp * 128 : nullptr;
-    rot = a.rotate != 0;
+    dst = a.q_rm + (int64_t)slot * a.Lp * 128;
   } else if (slot < a.nq + a.nkv) {
-    int j = slot - a.nq;
+    const int j = slot - a.nq;
     src = a.src_k + j * 128;
-    rm = a.k_rm ? a.k_rm + (int64_t)j * a.Lp * 128 : nullptr;
-    tr = a.k_t ? a.k_t + (int64_t)j * a.Lp * 128 : nullptr;
-    rot = a.rotate != 0;
+    dst = a.k_rm + (int64_t)j * a.Lp * 128;
   } else {
-    int j = slot - a.nq - a.nkv;
+    const int j = slot - a.nq - a.nkv;
     src = a.src_v + j * 128;
-    rm = a.v_rm ? a.v_rm + (int64_t)j * a.Lp * 128 : nullptr;
-    tr = a.v_t ? a.v_t + (int64_t)j * a.Lp * 128 : nullptr;
+    dst = a.v_rm + (int64_t)j * a.Lp * 128;
     rot = false;
+    is_v = true;
   }
   const int tid = threadIdx.x;
 #pragma unroll
@@ -66,7 +56,7 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a, RopeTable t) 
     u32x4 v = {0, 0, 0, 0};
     if (row < a.L) {
       v = *reinterpret_cast<const u32x4*>(src + row * a.src_ld + cc * 8);
-      if (rot) v = rotate8(v, t, row, cc * 4, false);
+      if (rot) v = rotate8(v, t, row, cc * 4);
       if (is_v && a.v_src_f16 && !a.v_out_f16) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(f16_lo(v[j]), f16_hi(v[j]));
@@ -75,34 +65,16 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a, RopeTable t) 
         for (int j = 0; j < 4; ++j) v[j] = pack_f16x2_sat(bf16_lo(v[j]), bf16_hi(v[j]));
       }
     }
-    if (rm) *reinterpret_cast<u32x4*>(rm + row * 128 + cc * 8) = v;
-    if (tr) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        tile[(cc * 8 + 2 * j) * T_PITCH + r] = (uint16_t)(v[j] & 0xffffu);
-        tile[(cc * 8 + 2 * j + 1) * T_PITCH + r] = (uint16_t)(v[j] >> 16);
-      }
-    }
-  }
-  if (!tr) return;
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    int c = tid + 256 * it;  // 128 d rows x 8 chunks of 8 positions
-    int dd = c >> 3, cc = c & 7;
-    u32x4 v = *reinterpret_cast<const u32x4*>(tile + dd * T_PITCH + cc * 8);
-    *reinterpret_cast<u32x4*>(tr + (int64_t)dd * a.Lp + r0 + cc * 8) = v;
+    *reinterpret_cast<u32x4*>(dst + row * 128 + cc * 8) = v;
   }
 }
 
 __global__ __launch_bounds__(256) void prep_dout_kernel(PrepDoutArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * T_PITCH];
   const int h = blockIdx.y;
   const int64_t r0 = (int64_t)blockIdx.x * ROWS;
   const uint16_t* src = a.src_do + h * 128;
   const uint16_t* o = a.o + h * 128;
   uint16_t* rm = a.do_rm + (int64_t)h * a.Lp * 128;
-  uint16_t* tr = a.do_t + (int64_t)h * a.Lp * 128;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
@@ -121,52 +93,11 @@ __global__ __launch_bounds__(256) void prep_dout_kernel(PrepDoutArgs a) {
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
     *reinterpret_cast<u32x4*>(rm + row * 128 + cc * 8) = v;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      tile[(cc * 8 + 2 * j) * T_PITCH + r] = (uint16_t)(v[j] & 0xffffu);
-      tile[(cc * 8 + 2 * j + 1) * T_PITCH + r] = (uint16_t)(v[j] >> 16);
-    }
     if (cc == 0) {
       a.dvec[(int64_t)h * a.Lp + row] = dot;
       a.lse2[(int64_t)h * a.Lp + row] = row < a.L ? a.lse[(int64_t)h * a.L + row] * kLog2e : 0.f;
     }
   }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    int c = tid + 256 * it;
-    int dd = c >> 3, cc = c & 7;
-    u32x4 v = *reinterpret_cast<const u32x4*>(tile + dd * T_PITCH + cc * 8);
-    *reinterpret_cast<u32x4*>(tr + (int64_t)dd * a.Lp + r0 + cc * 8) = v;
-  }
-}
-
-// one thread per (row, 8 columns) of one head
-__global__ __launch_bounds__(256) void dq_finalize_kernel(float* acc, int64_t L, int64_t Lp,
-                                                          float scale, uint16_t* dst, int64_t ld,
-                                                          RopeTable t) {
-  const int h = blockIdx.y;
-  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  int64_t row = idx >> 4;
-  int cc = (int)(idx & 15);
-  if (row >= Lp) return;
-  float* src = acc + ((int64_t)h * Lp + row) * 128 + cc * 8;
-  f32x4 a = *reinterpret_cast<f32x4*>(src);
-  f32x4 b = *reinterpret_cast<f32x4*>(src + 4);
-  *reinterpret_cast<f32x4*>(src) = f32x4{0, 0, 0, 0};
-  *reinterpret_cast<f32x4*>(src + 4) = f32x4{0, 0, 0, 0};
-  if (row >= L) return;
-  float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  u32x4 out;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float c, s;
-    rope_cos_sin(t, row, cc * 4 + j, c, s);
-    float e = v[2 * j] * scale, o = v[2 * j + 1] * scale;
-    // inverse rotation: angle -> -angle
-    out[j] = pack_bf16x2(e * c + o * s, -e * s + o * c);
-  }
-  *reinterpret_cast<u32x4*>(dst + row * ld + h * 128 + cc * 8) = out;
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(u32x4* p, int64_t n16) {
@@ -186,13 +117,6 @@ hipError_t launch_prep_qkv(const PrepArgs& a, const RopeTable& t, hipStream_t s)
 hipError_t launch_prep_dout(const PrepDoutArgs& a, hipStream_t s) {
   dim3 grid((unsigned)(a.Lp / ROWS), a.nh);
   hipLaunchKernelGGL(prep_dout_kernel, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_dq_finalize(float* dq_acc, int nh, int64_t L, int64_t Lp, float scale,
-                              uint16_t* dst, int64_t ld, const RopeTable& t, hipStream_t s) {
-  dim3 grid((unsigned)(Lp * 16 / 256), nh);
-  hipLaunchKernelGGL(dq_finalize_kernel, grid, dim3(256), 0, s, dq_acc, L, Lp, scale, dst, ld, t);
   return hipGetLastError();
 }
 

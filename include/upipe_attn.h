@@ -132,20 +132,22 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
  * upipe_attn_bwd with a pair of HIP events recorded on the caller's stream.
  * upipe_profile_read(kind, ...) waits for the recorded events and returns the
  * summed GPU milliseconds and the number of launches of one kernel class:
- *   UPIPE_KERNEL_ATTN_FWD  causal attention forward
- *   UPIPE_KERNEL_ATTN_BWD  causal attention backward
- *   UPIPE_KERNEL_GEMM      projection / gradient GEMMs
- *   UPIPE_KERNEL_PREP      RoPE / layout / dO preparation passes
- *   UPIPE_KERNEL_FINALIZE  dQ finalize, accumulator conversion, fills
+ *   UPIPE_KERNEL_ATTN_FWD      causal attention forward
+ *   UPIPE_KERNEL_ATTN_BWD_DKDV causal attention backward, dK and dV
+ *   UPIPE_KERNEL_ATTN_BWD_DQ   causal attention backward, dQ
+ *   UPIPE_KERNEL_GEMM          projection / gradient GEMMs
+ *   UPIPE_KERNEL_PREP          RoPE / layout / dO preparation passes
+ *   UPIPE_KERNEL_FINALIZE      accumulator conversion, fills
  * State is process-wide and not thread-safe.  Events are host-side HIP
  * objects; no device memory is allocated.  Returns UPIPE_OK, UPIPE_EINVAL
  * (bad kind or NULL output) or UPIPE_EHIP.
  */
 #define UPIPE_KERNEL_ATTN_FWD 0
-#define UPIPE_KERNEL_ATTN_BWD 1
-#define UPIPE_KERNEL_GEMM 2
-#define UPIPE_KERNEL_PREP 3
-#define UPIPE_KERNEL_FINALIZE 4
+#define UPIPE_KERNEL_ATTN_BWD_DKDV 1
+#define UPIPE_KERNEL_ATTN_BWD_DQ 2
+#define UPIPE_KERNEL_GEMM 3
+#define UPIPE_KERNEL_PREP 4
+#define UPIPE_KERNEL_FINALIZE 5
 int upipe_profile_enable(int on);
 int upipe_profile_read(int kind, double* total_ms, int64_t* launches);
 
