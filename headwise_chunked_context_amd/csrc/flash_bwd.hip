@@ -19,7 +19,8 @@
 //    tiles and share them in L2.  The next tile's loads are issued before the
 //    current tile's MFMAs.
 //  * dq: a workgroup owns 128 queries of one q head (4 waves x 32 queries)
-//    and walks the key tiles up to the diagonal like the forward kernel:
+//    and walks the key tiles up to the diagonal like the forward kernel
+//    (two workgroups per CU, single-buffered K/V tiles):
 //    S^T = K Q^T and dP^T = V dO^T give each lane ONE query (its LSE and D
 //    are per-lane scalars), dS^T feeds dQ^T = K^T dS^T as a B operand from
 //    registers and K^T is the transpose read of the same K tile.  The
@@ -216,11 +217,11 @@ constexpr int QBM = 128;       // queries per dq workgroup
 constexpr int QBN = 64;        // keys per dq step
 
 struct __attribute__((aligned(16))) DqSmem {
-  uint16_t K[2][QBN * 128];
-  uint16_t V[2][QBN * 128];
+  uint16_t K[QBN * 128];
+  uint16_t V[QBN * 128];
 };
 
-__global__ __launch_bounds__(256) void flash_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
   __shared__ DqSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -253,28 +254,23 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(BwdArgs a) {
   const int64_t kv_end = (q0 + QBM < a.L) ? q0 + QBM : a.L;
   const int n_kt = (int)((kv_end + QBN - 1) / QBN);
 
-  TileCopy<QBN> pk, pv;
-  auto load_kv = [&](int kt) {
-    const int64_t kk0 = (int64_t)kt * QBN;
-    pk.load(kp + kk0 * 128, tid);
-    pv.load(vp + kk0 * 128, tid);
-  };
-  auto store_kv = [&](int buf) {
-    pk.store(sm.K[buf], tid);
-    pv.store(sm.V[buf], tid);
-  };
-
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
   const float c = a.scale_log2;
 
-  load_kv(0);
-  store_kv(0);
-  __syncthreads();
+  // single-buffered K/V tiles: with two workgroups per CU the other
+  // workgroup's MFMAs cover this one's loads
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < n_kt) load_kv(kt + 1);
+    {
+      TileCopy<QBN> pk, pv;
+      pk.load(kp + (int64_t)kt * QBN * 128, tid);
+      pv.load(vp + (int64_t)kt * QBN * 128, tid);
+      __syncthreads();  // previous tile's reads are done
+      pk.store(sm.K, tid);
+      pv.store(sm.V, tid);
+      __syncthreads();
+    }
     const int64_t kstart = (int64_t)kt * QBN;
     if (kstart <= r0 + 31) {
       const bool need_mask = kstart + QBN - 1 > r0;
@@ -286,8 +282,8 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(BwdArgs a) {
         dp[kb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          sv[kb] = mfma32(tile_read_row(sm.K[cur], kb * 32 + l32, 2 * ks + g), qreg[ks], sv[kb]);
-          dp[kb] = mfma32(tile_read_row(sm.V[cur], kb * 32 + l32, 2 * ks + g), doreg[ks], dp[kb]);
+          sv[kb] = mfma32(tile_read_row(sm.K, kb * 32 + l32, 2 * ks + g), qreg[ks], sv[kb]);
+          dp[kb] = mfma32(tile_read_row(sm.V, kb * 32 + l32, 2 * ks + g), doreg[ks], dp[kb]);
         }
       }
       u32x4 pS[4];
@@ -311,11 +307,9 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(BwdArgs a) {
       for (int st = 0; st < 4; ++st) {
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          acc[db] = mfma32(tile_read_t(sm.K[cur], st * 16, db * 32, lane), pS[st], acc[db]);
+          acc[db] = mfma32(tile_read_t(sm.K, st * 16, db * 32, lane), pS[st], acc[db]);
       }
     }
-    if (kt + 1 < n_kt) store_kv(cur ^ 1);
-    __syncthreads();
   }
 
   if (my_q >= a.L) return;

@@ -9,7 +9,9 @@
 // Layout choices for CDNA4:
 //  * a workgroup is 4 waves x 32 query rows = 128 queries of one q head;
 //    key/value tiles of 64 keys are staged in LDS (double-buffered, loads
-//    for tile t+1 issued before the MFMAs of tile t);
+//    for tile t+1 issued before the MFMAs of tile t); registers are capped
+//    so that two workgroups share a CU (2 waves per SIMD), letting one
+//    wave's softmax run while the other's MFMAs do;
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: each lane then owns ONE query and 16 keys of
 //    a 32-key block, so the row max/sum need one cross-half exchange
@@ -35,7 +37,7 @@ namespace {
 constexpr int BM = 128;       // queries per workgroup
 constexpr int BN = 64;        // keys per step
 
-__global__ __launch_bounds__(256) void flash_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * 128];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * 128];
 
