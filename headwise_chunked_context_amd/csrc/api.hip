@@ -57,13 +57,14 @@ int check_shape(int64_t L, int32_t hidden, int32_t n_q, int32_t n_kv, int32_t he
 }
 
 // Split-K factor of the weight-gradient GEMMs (reduction over L): enough
-// workgroups to cover the 256 CUs twice, each split at least 256 rows.
+// 256 x 256 workgroups to cover the 256 CUs twice, each split at least 512
+// rows of the sequence.
 int dw_splits(int64_t L, int M, int N) {
-  int tiles = (M / 128) * (N / 128);
+  int tiles = ((M + 255) / 256) * ((N + 255) / 256);
   int s = (512 + tiles - 1) / tiles;
-  int max_by_len = (int)((L + 255) / 256);
+  int max_by_len = (int)((L + 511) / 512);
   if (s > max_by_len) s = max_by_len;
-  if (s > 16) s = 16;
+  if (s > 32) s = 32;
   if (s < 1) s = 1;
   return s;
 }

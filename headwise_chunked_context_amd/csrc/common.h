@@ -85,6 +85,18 @@ __device__ __forceinline__ u32x4 tile_read_t(const uint16_t* tile, int k0, int m
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Same, k in natural order: lane l gets rows {k0 + 8g + j, k0 + 8g + 4 + j},
+// i.e. k0 + 8g .. k0 + 8g + 7, the order of a row-per-lane operand.
+__device__ __forceinline__ u32x4 tile_read_t_nat(const uint16_t* tile, int k0, int m0, int lane) {
+  const int s = lane & 15, grp2 = (lane >> 4) & 1, g = lane >> 5;
+  const int col = m0 + 16 * grp2 + 4 * (s & 3);
+  const int chunk = col >> 3, half = (col & 7);
+  const int r0 = k0 + 8 * g + (s >> 2);
+  u32x2 lo = lds_read_tr16(tile + tile_off(r0, chunk) + half);
+  u32x2 hi = lds_read_tr16(tile + tile_off(r0 + 4, chunk) + half);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // Row-per-lane operand: row r, eight elements starting at column 8*chunk.
 __device__ __forceinline__ u32x4 tile_read_row(const uint16_t* tile, int row, int chunk) {
   return *reinterpret_cast<const u32x4*>(tile + tile_off(row, chunk));
