@@ -7,10 +7,11 @@
 //   dK = dS^T Q / sqrt(d),      D_i = dO_i . O_i.
 //
 // Two kernels, so that no gradient needs atomics:
-//  * dkdv: a workgroup owns 128 keys of one KV head (4 waves x 32 keys) and
-//    walks every q head of that KV group in the chunk and every 64-query tile
-//    at or below the diagonal, accumulating dK/dV of the group in fp32
-//    registers.  Scores are computed S = Q K^T so each lane owns ONE key:
+//  * dkdv: a workgroup owns 128 keys of one KV head (8 waves, two per SIMD:
+//    four 32-key blocks x two 32-query halves of every tile) and walks every
+//    q head of that KV group in the chunk and every 64-query tile at or
+//    below the diagonal, accumulating dK/dV of the group in fp32 registers;
+//    the two halves' partial sums meet in LDS once, at the end.  Scores are computed S = Q K^T so each lane owns ONE key:
 //    the S/dP accumulators feed dV^T = dO^T P and dK^T = Q^T dS as MFMA B
 //    operands straight from registers, with the dO^T / Q^T operands read
 //    from the row-major tiles by the LDS transpose read.  Query tiles are
@@ -37,36 +38,49 @@ namespace {
 
 constexpr int BNK = 128;       // keys per dkdv workgroup
 constexpr int BMQ = 64;        // queries per dkdv step
+constexpr int DKDV_THREADS = 512;
 
 struct __attribute__((aligned(16))) DkdvSmem {
-  uint16_t Q[BMQ * 128];
-  uint16_t dO[BMQ * 128];
-  float lse2[BMQ];
-  float dvec[BMQ];
+  uint16_t K[BNK * 128];        // the workgroup's K and V rows, loaded once
+  uint16_t V[BNK * 128];
+  uint16_t Q[2][BMQ * 128];     // double-buffered query tiles
+  uint16_t dO[2][BMQ * 128];
+  float lse2[2][BMQ];
+  float dvec[2][BMQ];
 };
+// the epilogue reuses the same LDS for the cross-wave reduction
+constexpr int kRedFloats = 4 * 64 * 64;
+static_assert(sizeof(DkdvSmem) >= kRedFloats * sizeof(float), "reduction buffer");
 
-__global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(BwdArgs a) {
+// 8 waves: wave w owns keys k0 + 32*(w%4) .. +32 and, of every 64-query
+// tile, the queries 32*(w/4) .. +32.  The two waves sharing a key block
+// hold partial dK/dV that are summed through LDS once at the end.
+__global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ DkdvSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int kwave = wave & 3, qh = wave >> 2;
   const int g = lane >> 5, l32 = lane & 31;
 
   const int kv = blockIdx.x % a.nkv;
   const int ktile = blockIdx.x / a.nkv;
   const int64_t k0 = (int64_t)ktile * BNK;
   if (k0 >= a.L) return;
-  const int64_t kw0 = k0 + 32 * wave;
+  const int64_t kw0 = k0 + 32 * kwave;
   const int64_t my_key = kw0 + l32;
 
   const uint16_t* kp = a.k + (int64_t)kv * a.Lp * 128;
   const uint16_t* vp = a.v + (int64_t)kv * a.Lp * 128;
 
-  // K and V of this lane's key as B operands (column = key, k = d)
-  u32x4 kreg[8], vreg[8];
+  // K and V rows of the workgroup into LDS: B operands (column = key,
+  // k = d) of S = Q K^T and dP = dO V^T, read back per step
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    kreg[ks] = *reinterpret_cast<const u32x4*>(kp + my_key * 128 + ks * 16 + g * 8);
-    vreg[ks] = *reinterpret_cast<const u32x4*>(vp + my_key * 128 + ks * 16 + g * 8);
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + DKDV_THREADS * i;
+    *reinterpret_cast<u32x4*>(&sm.K[tile_off(c >> 4, c & 15)]) =
+        *reinterpret_cast<const u32x4*>(kp + (k0 + (c >> 4)) * 128 + (c & 15) * 8);
+    *reinterpret_cast<u32x4*>(&sm.V[tile_off(c >> 4, c & 15)]) =
+        *reinterpret_cast<const u32x4*>(vp + (k0 + (c >> 4)) * 128 + (c & 15) * 8);
   }
 
   f32x16 acc_dk[4], acc_dv[4];
@@ -91,85 +105,119 @@ __global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(BwdArgs a) {
   auto step_head = [&](int s) { return j0 + s / steps_per_head; };
   auto step_tile = [&](int s) { return qs_hi - 1 - s % steps_per_head; };
 
-  TileCopy<BMQ> pq, pdo;
+  u32x4 pq[2], pdo[2];
   float plse = 0.f;
   auto load_step = [&](int s) {
     const int j = step_head(s);
     const int64_t q0 = (int64_t)step_tile(s) * BMQ;
-    pq.load(a.q + ((int64_t)j * a.Lp + q0) * 128, tid);
-    pdo.load(a.dO + ((int64_t)j * a.Lp + q0) * 128, tid);
+    const uint16_t* qsrc = a.q + ((int64_t)j * a.Lp + q0) * 128;
+    const uint16_t* dsrc = a.dO + ((int64_t)j * a.Lp + q0) * 128;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int cc = tid + DKDV_THREADS * i;
+      pq[i] = *reinterpret_cast<const u32x4*>(qsrc + (cc >> 4) * 128 + (cc & 15) * 8);
+      pdo[i] = *reinterpret_cast<const u32x4*>(dsrc + (cc >> 4) * 128 + (cc & 15) * 8);
+    }
     if (tid < BMQ) plse = a.lse2[(int64_t)j * a.Lp + q0 + tid];
     else if (tid < 2 * BMQ) plse = a.dvec[(int64_t)j * a.Lp + q0 + tid - BMQ];
   };
-  auto store_step = [&]() {
-    pq.store(sm.Q, tid);
-    pdo.store(sm.dO, tid);
-    if (tid < BMQ) sm.lse2[tid] = plse;
-    else if (tid < 2 * BMQ) sm.dvec[tid - BMQ] = plse;
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int cc = tid + DKDV_THREADS * i;
+      *reinterpret_cast<u32x4*>(&sm.Q[buf][tile_off(cc >> 4, cc & 15)]) = pq[i];
+      *reinterpret_cast<u32x4*>(&sm.dO[buf][tile_off(cc >> 4, cc & 15)]) = pdo[i];
+    }
+    if (tid < BMQ) sm.lse2[buf][tid] = plse;
+    else if (tid < 2 * BMQ) sm.dvec[buf][tid - BMQ] = plse;
   };
 
-  if (nsteps > 0) load_step(0);
+  if (nsteps > 0) {
+    load_step(0);
+    store_step(0);
+  }
+  __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
     const int64_t q0 = (int64_t)step_tile(s) * BMQ;
-    __syncthreads();  // previous step's LDS reads are done
-    store_step();
-    __syncthreads();
     if (s + 1 < nsteps) load_step(s + 1);  // in flight during this step's MFMAs
 
-    const bool need_mask = (q0 < k0 + BNK) || (q0 + BMQ > a.L);
-    // S = Q K^T and dP = dO V^T: element (query qb*32+acc_row(r,g), key my_key)
-    f32x16 sv[2], dp[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sv[qb] = f32x16{};
-      dp[qb] = f32x16{};
+    const int64_t qw0 = q0 + 32 * qh;        // this wave's first query
+    if (qw0 + 31 >= kw0) {                   // else every score is masked
+      const bool need_mask = (qw0 < kw0 + 32) || (qw0 + 32 > a.L);
+      const uint16_t* Qt = sm.Q[cur];
+      const uint16_t* dOt = sm.dO[cur];
+      // S = Q K^T and dP = dO V^T: element (query 32*qh + acc_row(r,g), key my_key)
+      f32x16 sv = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        sv[qb] = mfma32(tile_read_row(sm.Q, qb * 32 + l32, 2 * ks + g), kreg[ks], sv[qb]);
-        dp[qb] = mfma32(tile_read_row(sm.dO, qb * 32 + l32, 2 * ks + g), vreg[ks], dp[qb]);
+        sv = mfma32(tile_read_row(Qt, 32 * qh + l32, 2 * ks + g),
+                    tile_read_row(sm.K, 32 * kwave + l32, 2 * ks + g), sv);
+        dp = mfma32(tile_read_row(dOt, 32 * qh + l32, 2 * ks + g),
+                    tile_read_row(sm.V, 32 * kwave + l32, 2 * ks + g), dp);
       }
-    }
-    u32x4 pP[4], pS[4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
       float pv[16], dsv[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int qi = qb * 32 + r4 * 8 + g * 4;
-        f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[qi]);
-        f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dvec[qi]);
+        const int qi = 32 * qh + r4 * 8 + g * 4;
+        f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][qi]);
+        f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dvec[cur][qi]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = r4 * 4 + i;
-          float p = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], c, -l4[i]));
+          float p = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -l4[i]));
           if (need_mask) {
             const int64_t qrow = q0 + qi + i;
             if (my_key > qrow || qrow >= a.L) p = 0.f;
           }
           pv[r] = p;
-          dsv[r] = p * (dp[qb][r] - d4[i]);
+          dsv[r] = p * (dp[r] - d4[i]);
         }
       }
+      u32x4 pP[2], pS[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          pP[qb * 2 + h][t] = pack_bf16x2(pv[8 * h + 2 * t], pv[8 * h + 2 * t + 1]);
-          pS[qb * 2 + h][t] = pack_bf16x2(dsv[8 * h + 2 * t], dsv[8 * h + 2 * t + 1]);
+          pP[h][t] = pack_bf16x2(pv[8 * h + 2 * t], pv[8 * h + 2 * t + 1]);
+          pS[h][t] = pack_bf16x2(dsv[8 * h + 2 * t], dsv[8 * h + 2 * t + 1]);
         }
-      }
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS; B slot t of step st is query
-    // 16*st + 8*(t/4) + 4*g + t%4
+      // dV^T += dO^T P, dK^T += Q^T dS over this wave's 32 queries; B slot t
+      // of step h is query 32*qh + 16*h + 8*(t/4) + 4*g + t%4
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        acc_dv[db] = mfma32(tile_read_t(sm.dO, st * 16, db * 32, lane), pP[st], acc_dv[db]);
-        acc_dk[db] = mfma32(tile_read_t(sm.Q, st * 16, db * 32, lane), pS[st], acc_dk[db]);
-      }
+        for (int db = 0; db < 4; ++db) {
+          acc_dv[db] = mfma32(tile_read_t(dOt, 32 * qh + 16 * h, db * 32, lane), pP[h], acc_dv[db]);
+          acc_dk[db] = mfma32(tile_read_t(Qt, 32 * qh + 16 * h, db * 32, lane), pS[h], acc_dk[db]);
+        }
     }
+    if (s + 1 < nsteps) store_step(cur ^ 1);
+    __syncthreads();
   }
+
+  // ---- sum the two query halves' partial dK/dV (waves w and w+4)
+  float* red = reinterpret_cast<float*>(&sm);
+  float* mine = red + (kwave * 64) * 64 + lane;   // [kwave][reg][lane]
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    f32x16* acc = pass == 0 ? acc_dk : acc_dv;
+    if (qh == 1) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[(db * 16 + r) * 64] = acc[db][r];
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] += mine[(db * 16 + r) * 64];
+    }
+    __syncthreads();
+  }
+  if (qh == 1) return;
 
   // ---- epilogue: element (d = db*32 + acc_row(r,g), key my_key)
   if (my_key >= a.L) return;
@@ -338,7 +386,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
 
 hipError_t launch_flash_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.Lp / BNK) * a.nkv));
-  hipLaunchKernelGGL(flash_bwd_dkdv_kernel, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(flash_bwd_dkdv_kernel, grid, dim3(DKDV_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
