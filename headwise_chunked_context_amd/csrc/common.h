@@ -124,6 +124,34 @@ struct TileCopy {
   }
 };
 
+// Asynchronous global -> LDS copy (global_load_lds_dwordx4) of ROWS x 128
+// elements, rows 128 elements apart in global memory, into the swizzled
+// tile layout.  NWAVES waves split the work; each wave instruction moves
+// 64 x 16 bytes into 1 KB of consecutive LDS, so lane i fetches the global
+// chunk that the swizzle places at that position.  The caller waits with
+// lds_dma_wait() and a barrier before reading the tile.
+template <int ROWS, int NWAVES>
+__device__ __forceinline__ void tile_dma(uint16_t* tile, const uint16_t* src, int wave, int lane) {
+  constexpr int PER_WAVE = ROWS * 16 / 64 / NWAVES;
+  static_assert(PER_WAVE * 64 * NWAVES == ROWS * 16, "tile must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int n = wave * PER_WAVE + i;
+    const int q = n * 64 + lane;
+    const int row = q >> 4, chunk = (q & 15) ^ swz(q >> 4);
+    __builtin_amdgcn_global_load_lds(src + row * 128 + chunk * 8,
+                                     (__attribute__((address_space(3))) void*)(tile + n * 512),
+                                     16, 0, 0);
+  }
+}
+// 64 consecutive floats by one wave (global_load_lds_dword)
+__device__ __forceinline__ void vec64_dma(float* dst, const float* src, int lane) {
+  __builtin_amdgcn_global_load_lds(src + lane, (__attribute__((address_space(3))) void*)dst, 4, 0,
+                                   0);
+}
+// wait for this wave's outstanding vector-memory operations (vmcnt = 0)
+__device__ __forceinline__ void lds_dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};

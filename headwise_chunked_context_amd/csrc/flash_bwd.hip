@@ -11,14 +11,15 @@
 //    four 32-key blocks x two 32-query halves of every tile) and walks every
 //    q head of that KV group in the chunk and every 64-query tile at or
 //    below the diagonal, accumulating dK/dV of the group in fp32 registers;
-//    the two halves' partial sums meet in LDS once, at the end.  Scores are computed S = Q K^T so each lane owns ONE key:
-//    the S/dP accumulators feed dV^T = dO^T P and dK^T = Q^T dS as MFMA B
-//    operands straight from registers, with the dO^T / Q^T operands read
-//    from the row-major tiles by the LDS transpose read.  Query tiles are
-//    walked from the END of the sequence towards
-//    the diagonal, so workgroups that start together stream the same Q/dO
-//    tiles and share them in L2.  The next tile's loads are issued before the
-//    current tile's MFMAs.
+//    the two halves' partial sums meet in LDS once, at the end.  Scores are
+//    computed S = Q K^T so each lane owns ONE key: the S/dP accumulators
+//    feed dV^T = dO^T P and dK^T = Q^T dS as MFMA B operands straight from
+//    registers, with the dO^T / Q^T operands read from the row-major tiles
+//    by the LDS transpose read.  Query tiles are walked from the END of the
+//    sequence towards the diagonal (all of the group's heads per tile), so
+//    workgroups that run together stream the same Q/dO tiles in the same
+//    order and share them in L2.  The next tile arrives by asynchronous
+//    global->LDS loads issued before the current tile's MFMAs.
 //  * dq: a workgroup owns 128 queries of one q head (4 waves x 32 queries)
 //    and walks the key tiles up to the diagonal like the forward kernel
 //    (two workgroups per CU, single-buffered K/V tiles):
@@ -101,46 +102,31 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
   const int steps_per_head = qs_hi - qs_lo;
   const int nsteps = steps_per_head * (j1 - j0);
 
-  // step s -> (head j, query tile qs), tiles walked from the end backwards
-  auto step_head = [&](int s) { return j0 + s / steps_per_head; };
-  auto step_tile = [&](int s) { return qs_hi - 1 - s % steps_per_head; };
+  // step s -> (query tile qs, head j): tiles walked from the end backwards,
+  // all heads of the group per tile, so workgroups that run at the same
+  // time read the same Q/dO tiles in the same order (shared in L2) until
+  // each reaches its own diagonal
+  const int nheads = j1 - j0;
+  auto step_head = [&](int s) { return j0 + s % nheads; };
+  auto step_tile = [&](int s) { return qs_hi - 1 - s / nheads; };
 
-  u32x4 pq[2], pdo[2];
-  float plse = 0.f;
-  auto load_step = [&](int s) {
+  // the tiles of step s arrive in buffer s % 2 by asynchronous DMA
+  auto load_step = [&](int s, int buf) {
     const int j = step_head(s);
     const int64_t q0 = (int64_t)step_tile(s) * BMQ;
-    const uint16_t* qsrc = a.q + ((int64_t)j * a.Lp + q0) * 128;
-    const uint16_t* dsrc = a.dO + ((int64_t)j * a.Lp + q0) * 128;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int cc = tid + DKDV_THREADS * i;
-      pq[i] = *reinterpret_cast<const u32x4*>(qsrc + (cc >> 4) * 128 + (cc & 15) * 8);
-      pdo[i] = *reinterpret_cast<const u32x4*>(dsrc + (cc >> 4) * 128 + (cc & 15) * 8);
-    }
-    if (tid < BMQ) plse = a.lse2[(int64_t)j * a.Lp + q0 + tid];
-    else if (tid < 2 * BMQ) plse = a.dvec[(int64_t)j * a.Lp + q0 + tid - BMQ];
-  };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int cc = tid + DKDV_THREADS * i;
-      *reinterpret_cast<u32x4*>(&sm.Q[buf][tile_off(cc >> 4, cc & 15)]) = pq[i];
-      *reinterpret_cast<u32x4*>(&sm.dO[buf][tile_off(cc >> 4, cc & 15)]) = pdo[i];
-    }
-    if (tid < BMQ) sm.lse2[buf][tid] = plse;
-    else if (tid < 2 * BMQ) sm.dvec[buf][tid - BMQ] = plse;
+    tile_dma<BMQ, 8>(sm.Q[buf], a.q + ((int64_t)j * a.Lp + q0) * 128, wave, lane);
+    tile_dma<BMQ, 8>(sm.dO[buf], a.dO + ((int64_t)j * a.Lp + q0) * 128, wave, lane);
+    if (wave == 0) vec64_dma(sm.lse2[buf], a.lse2 + (int64_t)j * a.Lp + q0, lane);
+    if (wave == 1) vec64_dma(sm.dvec[buf], a.dvec + (int64_t)j * a.Lp + q0, lane);
   };
 
-  if (nsteps > 0) {
-    load_step(0);
-    store_step(0);
-  }
+  if (nsteps > 0) load_step(0, 0);
+  lds_dma_wait();
   __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
     const int cur = s & 1;
     const int64_t q0 = (int64_t)step_tile(s) * BMQ;
-    if (s + 1 < nsteps) load_step(s + 1);  // in flight during this step's MFMAs
+    if (s + 1 < nsteps) load_step(s + 1, cur ^ 1);  // lands during this step's MFMAs
 
     const int64_t qw0 = q0 + 32 * qh;        // this wave's first query
     if (qw0 + 31 >= kw0) {                   // else every score is masked
@@ -192,7 +178,7 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
           acc_dk[db] = mfma32(tile_read_t(Qt, 32 * qh + 16 * h, db * 32, lane), pS[h], acc_dk[db]);
         }
     }
-    if (s + 1 < nsteps) store_step(cur ^ 1);
+    lds_dma_wait();
     __syncthreads();
   }
 
