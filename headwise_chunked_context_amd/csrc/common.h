@@ -45,6 +45,12 @@ __device__ __forceinline__ f32x16 mfma32_f16(const u32x4& a, const u32x4& b, con
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// Combine a per-lane value with the one of the lane in the other 32-lane half
+// (lane ^ 32).  A single bpermute; the permlane32 swap builtin is not used
+// because the optimizer folds its two results into one.
+__device__ __forceinline__ float half_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float half_sum(float x) { return x + __shfl_xor(x, 32); }
+
 // Row of the 32x32 accumulator element held in register r by a lane of half g.
 __device__ __forceinline__ int acc_row(int r, int g) { return (r >> 2) * 8 + g * 4 + (r & 3); }
 

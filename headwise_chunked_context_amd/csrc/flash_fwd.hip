@@ -26,6 +26,8 @@
 //    bf16): P lies in [0, 1] and fp16's 10-bit mantissa keeps the forward
 //    output inside its error budget where bf16's 7 bits do not;
 //  * the softmax runs in base 2 with the 1/sqrt(d) scale folded into one FMA;
+//    the running maximum is raised lazily (only when a score exceeds it by
+//    more than 2^8), which removes the per-tile rescale of O;
 //  * workgroups are issued heaviest (last query tile) first, and consecutive
 //    workgroups take different heads of the chunk so the heads sharing a KV
 //    group spread over the XCDs while each XCD streams one head's K/V.
@@ -112,15 +114,25 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
             if (key > my_q) s[kb][r] = -__builtin_inff();
           }
       }
-      float mx = -__builtin_inff();
+      // running maximum, raised lazily: only when some row's new score
+      // exceeds it by more than 2^8 in the exponent (wave-uniform), so the
+      // 64-register rescale of O runs a few times per row instead of every
+      // tile; in between P <= 256, well inside fp16 and fp32
+      float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      const float mc = m_new * c;
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
+      mx = half_max(mx);
+      if (__builtin_amdgcn_ballot_w64(mx * c > fmaf(m_run, c, 8.f))) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc_o[db] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = m_run * c;
       float rsum = 0.f;
       u32x4 pb[4];
 #pragma unroll
@@ -139,10 +151,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
           pb[kb * 2 + h][3] = pack_f16x2(p[8 * h + 6], p[8 * h + 7]);
         }
       }
-      l_run = l_run * alpha + rsum;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) acc_o[db] *= alpha;
+      l_run += rsum;
       // O^T += V^T P^T; B slot t of step st is key 16*st + 8*(t/4) + 4*g + t%4
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_sum(l_run);
   if (my_q >= a.L) return;
   const float inv = 1.f / l_tot;
   const int hg = a.q_head0 + head;
