@@ -28,6 +28,9 @@ HIPCC_FLAGS = [
     "-munsafe-fp-atomics",
     # packed fp32 VALU ops stay off (v_pk_*_f32); plain scalar float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # device code never relies on NaN semantics (masked scores are -inf, not
+    # NaN); this lets fmaxf lower to v_max/v_max3 without quieting its inputs
+    "-Xarch_device", "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]

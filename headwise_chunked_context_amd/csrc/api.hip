@@ -345,6 +345,7 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pa.rotate = s.proj ? 0 : 1;
     pa.v_src_f16 = s.proj ? 1 : 0;
     pa.v_out_f16 = 1;
+    pa.v_tiles = 1;
     UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_qkv(pa, rope, st));
 
     // 2. causal attention of the chunk's heads; stores O and LSE

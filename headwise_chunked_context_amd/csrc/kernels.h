@@ -69,6 +69,8 @@ struct PrepArgs {
   int rotate;              // apply RoPE to q and k heads
   int v_src_f16;           // v source holds fp16 bits (else bf16)
   int v_out_f16;           // write v as fp16 (else bf16)
+  int v_tiles;             // write v (fp16) as the forward's transposed
+                           // 64-key tiles instead of row-major (see prep.hip)
 };
 hipError_t launch_prep_qkv(const PrepArgs& a, const RopeTable& t, hipStream_t s);
 
@@ -94,7 +96,7 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 struct FwdArgs {
   const uint16_t* q;    // [nh][Lp][128], rotated
   const uint16_t* k;    // [nkv][Lp][128], rotated
-  const uint16_t* v;    // [nkv][Lp][128] fp16
+  const uint16_t* v;    // [nkv][Lp/64] transposed fp16 tiles of 128 x 64 (prep.hip)
   int nh;               // query heads in this chunk
   int group;            // G = Hq / Hkv
   int q_head0;          // global index of the chunk's first q head

@@ -1,7 +1,8 @@
 // Memory-bound passes around the attention kernels (gfx950):
 //   prep_qkv    head-major copies of a chunk's q/k/v, RoPE on q and k,
 //               zero padding to Lp rows, v converted between bf16 and fp16
-//               as the consumer needs;
+//               as the consumer needs; for the forward, v goes out as
+//               transposed 64-key tiles (below);
 //   prep_dout   the same for dO, plus D_i = dO_i . O_i and LSE in base 2;
 //   zero        fill kernel (used instead of hipMemsetAsync).
 // Each workgroup owns 64 rows x 128 columns of one head: coalesced 16-byte
@@ -26,6 +27,51 @@ __device__ __forceinline__ u32x4 rotate8(u32x4 v, const RopeTable& t, int64_t po
   return out;
 }
 
+// The forward's V operand: for every 64 keys one 128 x 64 fp16 tile of V^T
+// (row = d, 128 bytes per row), stored exactly as the LDS tile the forward
+// kernel reads, so the kernel copies it with contiguous 16-byte loads:
+//  * the 16-byte chunk c = 2*st + g of row d holds keys 16st + 4g + {0..3}
+//    followed by 16st + 8 + 4g + {0..3}: the key order in which the score
+//    accumulator hands P^T to the O^T = V^T P^T MFMA as its B operand;
+//  * chunk c of row d sits at position c ^ ((d >> 1) & 7), which makes the
+//    kernel's row-per-lane 16-byte reads of 16 consecutive rows hit 16
+//    different 16-byte bank groups.
+__device__ void write_v_tiles(const PrepArgs& a, const uint16_t* src, uint16_t* dst, int64_t r0,
+                              int tid) {
+  __shared__ __attribute__((aligned(16))) uint16_t vs[ROWS][136];  // [key][d] fp16 bits
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    int c = tid + 256 * it;
+    int r = c >> 4, cc = c & 15;
+    int64_t row = r0 + r;
+    u32x4 v = {0, 0, 0, 0};
+    if (row < a.L) {
+      v = *reinterpret_cast<const u32x4*>(src + row * a.src_ld + cc * 8);
+      if (!a.v_src_f16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = pack_f16x2_sat(bf16_lo(v[j]), bf16_hi(v[j]));
+      }
+    }
+    *reinterpret_cast<u32x4*>(&vs[r][cc * 8]) = v;
+  }
+  __syncthreads();
+  uint16_t* tile = dst + r0 * 128;  // tile r0 / 64 of the head
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    int q = tid + 256 * it;  // 16-byte position in the tile
+    int d = q >> 3;
+    int c = (q & 7) ^ ((d >> 1) & 7);
+    int kb = (c >> 1) * 16 + (c & 1) * 4;
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      w[j] = (uint32_t)vs[kb + 2 * j][d] | ((uint32_t)vs[kb + 2 * j + 1][d] << 16);
+      w[2 + j] = (uint32_t)vs[kb + 8 + 2 * j][d] | ((uint32_t)vs[kb + 8 + 2 * j + 1][d] << 16);
+    }
+    *reinterpret_cast<u32x4*>(tile + q * 8) = w;
+  }
+}
+
 // one workgroup per 64 rows of one head slot (q heads, then k, then v)
 __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a, RopeTable t) {
   const int slot = blockIdx.y;
@@ -48,6 +94,10 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a, RopeTable t) 
     is_v = true;
   }
   const int tid = threadIdx.x;
+  if (is_v && a.v_tiles) {  // uniform: the whole workgroup has one slot
+    write_v_tiles(a, src, dst, r0, tid);
+    return;
+  }
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     int c = tid + 256 * it;  // 64 rows x 16 chunks of 8
