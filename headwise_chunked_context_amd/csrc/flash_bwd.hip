@@ -41,47 +41,93 @@ constexpr int BNK = 128;       // keys per dkdv workgroup
 constexpr int BMQ = 64;        // queries per dkdv step
 constexpr int DKDV_THREADS = 512;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// The query tiles are double-buffered in distinct fields (the step loop is
+// unrolled by two), so every LDS address is a per-lane base plus an
+// immediate and reads of one buffer are visibly independent of the copy in
+// flight into the other.  The per-step buffers come first: LDS immediates
+// reach 64 KB.  The workgroup's K and V rows, loaded once, come last.
 struct __attribute__((aligned(16))) DkdvSmem {
-  uint16_t K[BNK * 128];        // the workgroup's K and V rows, loaded once
+  float L0[BMQ], L1[BMQ];           // LSE of the tile's rows (base 2)
+  float E0[BMQ], E1[BMQ];           // D = dO . O of the tile's rows
+  uint16_t Q0[BMQ * 128], Q1[BMQ * 128];
+  uint16_t O0[BMQ * 128], O1[BMQ * 128];  // dO tiles
+  uint16_t K[BNK * 128];
   uint16_t V[BNK * 128];
-  uint16_t Q[2][BMQ * 128];     // double-buffered query tiles
-  uint16_t dO[2][BMQ * 128];
-  float lse2[2][BMQ];
-  float dvec[2][BMQ];
 };
-// the epilogue reuses the same LDS for the cross-wave reduction
-constexpr int kRedFloats = 4 * 64 * 64;
-static_assert(sizeof(DkdvSmem) >= kRedFloats * sizeof(float), "reduction buffer");
 
 // 8 waves: wave w owns keys k0 + 32*(w%4) .. +32 and, of every 64-query
 // tile, the queries 32*(w/4) .. +32.  The two waves sharing a key block
 // hold partial dK/dV that are summed through LDS once at the end.
 __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ DkdvSmem sm;
+  float* const L0 = sm.L0;
+  float* const L1 = sm.L1;
+  float* const E0 = sm.E0;
+  float* const E1 = sm.E1;
+  uint16_t* const Q0 = sm.Q0;
+  uint16_t* const Q1 = sm.Q1;
+  uint16_t* const O0 = sm.O0;
+  uint16_t* const O1 = sm.O1;
+  uint16_t* const Ks = sm.K;
+  uint16_t* const Vs = sm.V;
+
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kwave = wave & 3, qh = wave >> 2;
   const int g = lane >> 5, l32 = lane & 31;
 
   const int kv = blockIdx.x % a.nkv;
   const int ktile = blockIdx.x / a.nkv;
-  const int64_t k0 = (int64_t)ktile * BNK;
+  const int k0 = ktile * BNK;
   if (k0 >= a.L) return;
-  const int64_t kw0 = k0 + 32 * kwave;
-  const int64_t my_key = kw0 + l32;
+  const int L = (int)a.L;
+  const int kw0 = k0 + 32 * kwave;
+  const int my_key = kw0 + l32;
 
-  const uint16_t* kp = a.k + (int64_t)kv * a.Lp * 128;
-  const uint16_t* vp = a.v + (int64_t)kv * a.Lp * 128;
+  const uint16_t* kp = a.k + ((int64_t)kv * a.Lp + k0) * 128;
+  const uint16_t* vp = a.v + ((int64_t)kv * a.Lp + k0) * 128;
 
-  // K and V rows of the workgroup into LDS: B operands (column = key,
-  // k = d) of S = Q K^T and dP = dO V^T, read back per step
+  // K and V rows of the workgroup -> LDS (swizzled), 4 KB per wave each
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = tid + DKDV_THREADS * i;
-    *reinterpret_cast<u32x4*>(&sm.K[tile_off(c >> 4, c & 15)]) =
-        *reinterpret_cast<const u32x4*>(kp + (k0 + (c >> 4)) * 128 + (c & 15) * 8);
-    *reinterpret_cast<u32x4*>(&sm.V[tile_off(c >> 4, c & 15)]) =
-        *reinterpret_cast<const u32x4*>(vp + (k0 + (c >> 4)) * 128 + (c & 15) * 8);
+    const int n = wave * 4 + i;
+    const int row = 4 * n + (lane >> 4);
+    const uint32_t off = (uint32_t)(row * 128 + (((lane & 15) ^ swz(row)) << 3));
+    __builtin_amdgcn_global_load_lds(kp + off, (lds_void*)(Ks + n * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vp + off, (lds_void*)(Vs + n * 512), 16, 0, 0);
+  }
+
+  // per-lane element offsets, fixed for the whole loop
+  //  row-per-lane operands: Q/dO rows 32*qh + l32, chunk 2ks + g; the K/V
+  //  rows 32*kwave + l32 sit a uniform distance dko further (same swizzle)
+  int offq[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) offq[ks] = tile_off(32 * qh + l32, 2 * ks + g);
+  const int dko_init = (kwave - qh) * 32 * 128;
+  //  transposed operands dO^T / Q^T (see tile_read_t): column block db,
+  //  rows 32*qh + 4g + (lane%16)/4 and +8; 16h more rows are an immediate
+  int offt[4][2];
+  {
+    const int sl = lane & 15, grp2 = (lane >> 4) & 1;
+    const int r0 = 32 * qh + 4 * g + (sl >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int col = db * 32 + 16 * grp2 + 4 * (sl & 3);
+      offt[db][0] = tile_off(r0, col >> 3) + (col & 7);
+      offt[db][1] = tile_off(r0 + 8, col >> 3) + (col & 7);
+    }
+  }
+  //  per-row scalars of the lane's queries 32*qh + 8*r4 + 4g + i
+  const int offl = 32 * qh + 4 * g;
+  //  query tile copy: wave w moves rows 8w .. 8w+7 of the Q and dO tiles
+  uint32_t qdma[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * wave + 4 * i + (lane >> 4);
+    qdma[i] = (uint32_t)(row * 128 + (((lane & 15) ^ swz(row)) << 3));
   }
 
   f32x16 acc_dk[4], acc_dv[4];
@@ -97,116 +143,142 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
   int j1 = j0 + a.group;
   if (j0 < 0) j0 = 0;
   if (j1 > a.nh) j1 = a.nh;
-  const int qs_lo = (int)(k0 / BMQ);                 // first tile that sees these keys
-  const int qs_hi = (int)((a.L + BMQ - 1) / BMQ);    // one past the last tile
-  const int steps_per_head = qs_hi - qs_lo;
-  const int nsteps = steps_per_head * (j1 - j0);
+  const int qs_lo = k0 / BMQ;                 // first tile that sees these keys
+  const int qs_hi = (L + BMQ - 1) / BMQ;      // one past the last tile
+  const int nsteps = (qs_hi - qs_lo) * (j1 - j0);
 
-  // step s -> (query tile qs, head j): tiles walked from the end backwards,
-  // all heads of the group per tile, so workgroups that run at the same
-  // time read the same Q/dO tiles in the same order (shared in L2) until
-  // each reaches its own diagonal
-  const int nheads = j1 - j0;
-  auto step_head = [&](int s) { return j0 + s % nheads; };
-  auto step_tile = [&](int s) { return qs_hi - 1 - s / nheads; };
-
-  // the tiles of step s arrive in buffer s % 2 by asynchronous DMA
-  auto load_step = [&](int s, int buf) {
-    const int j = step_head(s);
-    const int64_t q0 = (int64_t)step_tile(s) * BMQ;
-    tile_dma<BMQ, 8>(sm.Q[buf], a.q + ((int64_t)j * a.Lp + q0) * 128, wave, lane);
-    tile_dma<BMQ, 8>(sm.dO[buf], a.dO + ((int64_t)j * a.Lp + q0) * 128, wave, lane);
-    if (wave == 0) vec64_dma(sm.lse2[buf], a.lse2 + (int64_t)j * a.Lp + q0, lane);
-    if (wave == 1) vec64_dma(sm.dvec[buf], a.dvec + (int64_t)j * a.Lp + q0, lane);
+  // Steps walk the query tiles from the end of the sequence backwards, all
+  // heads of the group per tile, so workgroups that run at the same time
+  // read the same Q/dO tiles in the same order (shared in L2) until each
+  // reaches its own diagonal.  (j, qt) is the step being loaded.
+  int ld_j = j0, ld_qt = qs_hi - 1;
+  auto load_next = [&](uint16_t* Qd, uint16_t* Od, float* Ld, float* Ed) {
+    const int64_t base = (int64_t)ld_j * a.Lp + ld_qt * BMQ;
+    const uint16_t* qsrc = a.q + base * 128;
+    const uint16_t* osrc = a.dO + base * 128;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_global_load_lds(qsrc + qdma[i], (lds_void*)(Qd + (wave * 2 + i) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(osrc + qdma[i], (lds_void*)(Od + (wave * 2 + i) * 512), 16, 0, 0);
+    }
+    if (wave == 0) __builtin_amdgcn_global_load_lds(a.lse2 + base + lane, (lds_void*)Ld, 4, 0, 0);
+    if (wave == 1) __builtin_amdgcn_global_load_lds(a.dvec + base + lane, (lds_void*)Ed, 4, 0, 0);
+    if (++ld_j == j1) {
+      ld_j = j0;
+      --ld_qt;
+    }
   };
 
-  if (nsteps > 0) load_step(0, 0);
+  auto step = [&](int qt, const uint16_t* Qt, const uint16_t* Ot, const float* Lt, const float* Et) {
+    const int q0 = qt * BMQ;
+    const int qw0 = q0 + 32 * qh;            // this wave's first query
+    if (qw0 + 31 < kw0) return;              // every score is masked
+    const bool need_mask = (qw0 < kw0 + 32) || (qw0 + 32 > L);
+    // S = Q K^T and dP = dO V^T: element (query 32*qh + acc_row(r,g), key my_key)
+    f32x16 sv = f32x16{}, dp = f32x16{};
+    // K/V addresses are rebuilt every step (8 adds) rather than held in 8
+    // more registers
+    int dko = dko_init;
+    asm volatile("" : "+s"(dko));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int ok = offq[ks] + dko;
+      sv = mfma32(*reinterpret_cast<const u32x4*>(Qt + offq[ks]),
+                  *reinterpret_cast<const u32x4*>(Ks + ok), sv);
+      dp = mfma32(*reinterpret_cast<const u32x4*>(Ot + offq[ks]),
+                  *reinterpret_cast<const u32x4*>(Vs + ok), dp);
+    }
+    if (need_mask) {  // key after the query, or a padding query row
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = q0 + 32 * qh + acc_row(r, g);
+        if (my_key > qrow || qrow >= L) sv[r] = -__builtin_inff();
+      }
+    }
+    u32x4 pP[2], pS[2];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + offl + 8 * r4);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(Et + offl + 8 * r4);
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r4 * 4 + i;
+        pv[i] = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -l4[i]));
+        dsv[i] = pv[i] * (dp[r] - d4[i]);
+      }
+      // registers r4*4 .. +3 are B slots 4*(r4%2) .. +3 of step r4/2
+      pP[r4 >> 1][2 * (r4 & 1)] = pack_bf16x2(pv[0], pv[1]);
+      pP[r4 >> 1][2 * (r4 & 1) + 1] = pack_bf16x2(pv[2], pv[3]);
+      pS[r4 >> 1][2 * (r4 & 1)] = pack_bf16x2(dsv[0], dsv[1]);
+      pS[r4 >> 1][2 * (r4 & 1) + 1] = pack_bf16x2(dsv[2], dsv[3]);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over this wave's 32 queries; B slot t
+    // of step h is query 32*qh + 16*h + 8*(t/4) + 4*g + t%4
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const u32x2 o_lo = lds_read_tr16(Ot + offt[db][0] + h * 2048);
+        const u32x2 o_hi = lds_read_tr16(Ot + offt[db][1] + h * 2048);
+        acc_dv[db] = mfma32(u32x4{o_lo[0], o_lo[1], o_hi[0], o_hi[1]}, pP[h], acc_dv[db]);
+        const u32x2 q_lo = lds_read_tr16(Qt + offt[db][0] + h * 2048);
+        const u32x2 q_hi = lds_read_tr16(Qt + offt[db][1] + h * 2048);
+        acc_dk[db] = mfma32(u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}, pS[h], acc_dk[db]);
+      }
+  };
+
+  if (nsteps > 0) load_next(Q0, O0, L0, E0);
   lds_dma_wait();
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    const int64_t q0 = (int64_t)step_tile(s) * BMQ;
-    if (s + 1 < nsteps) load_step(s + 1, cur ^ 1);  // lands during this step's MFMAs
-
-    const int64_t qw0 = q0 + 32 * qh;        // this wave's first query
-    if (qw0 + 31 >= kw0) {                   // else every score is masked
-      const bool need_mask = (qw0 < kw0 + 32) || (qw0 + 32 > a.L);
-      const uint16_t* Qt = sm.Q[cur];
-      const uint16_t* dOt = sm.dO[cur];
-      // S = Q K^T and dP = dO V^T: element (query 32*qh + acc_row(r,g), key my_key)
-      f32x16 sv = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        sv = mfma32(tile_read_row(Qt, 32 * qh + l32, 2 * ks + g),
-                    tile_read_row(sm.K, 32 * kwave + l32, 2 * ks + g), sv);
-        dp = mfma32(tile_read_row(dOt, 32 * qh + l32, 2 * ks + g),
-                    tile_read_row(sm.V, 32 * kwave + l32, 2 * ks + g), dp);
-      }
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int qi = 32 * qh + r4 * 8 + g * 4;
-        f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][qi]);
-        f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dvec[cur][qi]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = r4 * 4 + i;
-          float p = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -l4[i]));
-          if (need_mask) {
-            const int64_t qrow = q0 + qi + i;
-            if (my_key > qrow || qrow >= a.L) p = 0.f;
-          }
-          pv[r] = p;
-          dsv[r] = p * (dp[r] - d4[i]);
-        }
-      }
-      u32x4 pP[2], pS[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          pP[h][t] = pack_bf16x2(pv[8 * h + 2 * t], pv[8 * h + 2 * t + 1]);
-          pS[h][t] = pack_bf16x2(dsv[8 * h + 2 * t], dsv[8 * h + 2 * t + 1]);
-        }
-      // dV^T += dO^T P, dK^T += Q^T dS over this wave's 32 queries; B slot t
-      // of step h is query 32*qh + 16*h + 8*(t/4) + 4*g + t%4
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          acc_dv[db] = mfma32(tile_read_t(dOt, 32 * qh + 16 * h, db * 32, lane), pP[h], acc_dv[db]);
-          acc_dk[db] = mfma32(tile_read_t(Qt, 32 * qh + 16 * h, db * 32, lane), pS[h], acc_dk[db]);
-        }
+  int qt = qs_hi - 1, hj = j0;  // step being computed: tile qt, head hj
+  auto advance = [&]() {
+    if (++hj == j1) {
+      hj = j0;
+      --qt;
     }
+  };
+  for (int s = 0; s < nsteps; s += 2) {
+    if (s + 1 < nsteps) load_next(Q1, O1, L1, E1);  // lands during this step's MFMAs
+    step(qt, Q0, O0, L0, E0);
+    advance();
+    lds_dma_wait();
+    __syncthreads();
+    if (s + 1 >= nsteps) break;
+    if (s + 2 < nsteps) load_next(Q0, O0, L0, E0);
+    step(qt, Q1, O1, L1, E1);
+    advance();
     lds_dma_wait();
     __syncthreads();
   }
+  (void)hj;
 
-  // ---- sum the two query halves' partial dK/dV (waves w and w+4)
-  float* red = reinterpret_cast<float*>(&sm);
-  float* mine = red + (kwave * 64) * 64 + lane;   // [kwave][reg][lane]
+  // ---- sum the two query halves' partial dK/dV (waves w and w+4), half
+  // of one accumulator set per pass through the K rows' LDS
+  float* red = reinterpret_cast<float*>(sm.K);
+  float* mine = red + (kwave * 32) * 64 + lane;   // [kwave][reg][lane]
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    f32x16* acc = pass == 0 ? acc_dk : acc_dv;
+  for (int pass = 0; pass < 4; ++pass) {
+    f32x16* acc = (pass < 2 ? acc_dk : acc_dv) + 2 * (pass & 1);
+    __syncthreads();
     if (qh == 1) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mine[(db * 16 + r) * 64] = acc[db][r];
     }
     __syncthreads();
     if (qh == 0) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] += mine[(db * 16 + r) * 64];
     }
-    __syncthreads();
   }
   if (qh == 1) return;
 
   // ---- epilogue: element (d = db*32 + acc_row(r,g), key my_key)
-  if (my_key >= a.L) return;
+  if (my_key >= L) return;
   float* dka = a.dk_acc + ((int64_t)kv * a.Lp + my_key) * 128;
   float* dva = a.dv_acc + ((int64_t)kv * a.Lp + my_key) * 128;
 #pragma unroll
@@ -241,8 +313,8 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
       }
       u32x2 wk = {pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3])};
       u32x2 wv = {pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
-      *reinterpret_cast<u32x2*>(a.dk_out + my_key * a.out_ld + (int64_t)kv * 128 + d) = wk;
-      *reinterpret_cast<u32x2*>(a.dv_out + my_key * a.out_ld + (int64_t)kv * 128 + d) = wv;
+      *reinterpret_cast<u32x2*>(a.dk_out + (int64_t)my_key * a.out_ld + (int64_t)kv * 128 + d) = wk;
+      *reinterpret_cast<u32x2*>(a.dv_out + (int64_t)my_key * a.out_ld + (int64_t)kv * 128 + d) = wv;
     }
 }
 
