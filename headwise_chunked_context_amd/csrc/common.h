@@ -150,6 +150,37 @@ __device__ __forceinline__ void tile_dma(uint16_t* tile, const uint16_t* src, in
                                      16, 0, 0);
   }
 }
+// The same copy issued as inline asm (16 or 4 bytes per lane; M0 = LDS
+// destination of lane 0).  The compiler then does not know that a copy into
+// LDS is in flight, so it does not make later LDS reads wait for it: it
+// cannot tell the two buffers of a double-buffered loop apart for every read
+// form (transpose reads in particular) and would otherwise wait for the
+// copy into the other buffer before each of them.  The caller owns
+// completion: lds_dma_wait() and a barrier before the destination is read,
+// and no copy into a buffer until every wave has passed the barrier that
+// follows its last read.  M0 is listed as clobbered; the compiler keeps no
+// value in it across other code (it sets M0 right before each of its own
+// uses), which the warning about clobbering a reserved register concerns.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_untracked(const void* src, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_dst)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_untracked(const void* src, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(lds_dst)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // 64 consecutive floats by one wave (global_load_lds_dword)
 __device__ __forceinline__ void vec64_dma(float* dst, const float* src, int lane) {
   __builtin_amdgcn_global_load_lds(src + lane, (__attribute__((address_space(3))) void*)dst, 4, 0,

@@ -96,8 +96,8 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
     const int n = wave * 4 + i;
     const int row = 4 * n + (lane >> 4);
     const uint32_t off = (uint32_t)(row * 128 + (((lane & 15) ^ swz(row)) << 3));
-    __builtin_amdgcn_global_load_lds(kp + off, (lds_void*)(Ks + n * 512), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vp + off, (lds_void*)(Vs + n * 512), 16, 0, 0);
+    dma16_untracked(kp + off, lds_addr(Ks + n * 512));
+    dma16_untracked(vp + off, lds_addr(Vs + n * 512));
   }
 
   // per-lane element offsets, fixed for the whole loop
@@ -158,11 +158,11 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
     const uint16_t* osrc = a.dO + base * 128;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_global_load_lds(qsrc + qdma[i], (lds_void*)(Qd + (wave * 2 + i) * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(osrc + qdma[i], (lds_void*)(Od + (wave * 2 + i) * 512), 16, 0, 0);
+      dma16_untracked(qsrc + qdma[i], lds_addr(Qd + (wave * 2 + i) * 512));
+      dma16_untracked(osrc + qdma[i], lds_addr(Od + (wave * 2 + i) * 512));
     }
-    if (wave == 0) __builtin_amdgcn_global_load_lds(a.lse2 + base + lane, (lds_void*)Ld, 4, 0, 0);
-    if (wave == 1) __builtin_amdgcn_global_load_lds(a.dvec + base + lane, (lds_void*)Ed, 4, 0, 0);
+    if (wave == 0) dma4_untracked(a.lse2 + base + lane, lds_addr(Ld));
+    if (wave == 1) dma4_untracked(a.dvec + base + lane, lds_addr(Ed));
     if (++ld_j == j1) {
       ld_j = j0;
       --ld_qt;
@@ -322,105 +322,154 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
 constexpr int QBM = 128;       // queries per dq workgroup
 constexpr int QBN = 64;        // keys per dq step
 
+// K and V tiles double-buffered in distinct fields (the key loop is unrolled
+// by two): every LDS address is a per-lane base plus an immediate.
 struct __attribute__((aligned(16))) DqSmem {
-  uint16_t K[QBN * 128];
-  uint16_t V[QBN * 128];
+  uint16_t K0[QBN * 128], V0[QBN * 128];
+  uint16_t K1[QBN * 128], V1[QBN * 128];
 };
 
 __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
   __shared__ DqSmem sm;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
 
   const int nqt = (int)(a.Lp / QBM);
   const int head = blockIdx.x % a.nh;
   const int qt = nqt - 1 - (int)(blockIdx.x / a.nh);
-  const int64_t q0 = (int64_t)qt * QBM;
+  const int q0 = qt * QBM;
   if (q0 >= a.L) return;
+  const int L = (int)a.L;
   const int kvh = (a.q_head0 + head) / a.group - a.kv_head0;
   const uint16_t* qp = a.q + (int64_t)head * a.Lp * 128;
   const uint16_t* dop = a.dO + (int64_t)head * a.Lp * 128;
   const uint16_t* kp = a.k + (int64_t)kvh * a.Lp * 128;
   const uint16_t* vp = a.v + (int64_t)kvh * a.Lp * 128;
 
-  const int64_t r0 = q0 + 32 * wave;
-  const int64_t my_q = r0 + l32;
+  const int r0 = q0 + 32 * wave;
+  const int my_q = r0 + l32;
 
   // Q and dO of this lane's query as B operands (column = query, k = d)
   u32x4 qreg[8], doreg[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    qreg[ks] = *reinterpret_cast<const u32x4*>(qp + my_q * 128 + ks * 16 + g * 8);
-    doreg[ks] = *reinterpret_cast<const u32x4*>(dop + my_q * 128 + ks * 16 + g * 8);
+    qreg[ks] = *reinterpret_cast<const u32x4*>(qp + (int64_t)my_q * 128 + ks * 16 + g * 8);
+    doreg[ks] = *reinterpret_cast<const u32x4*>(dop + (int64_t)my_q * 128 + ks * 16 + g * 8);
   }
   const float lse2 = a.lse2[(int64_t)head * a.Lp + my_q];
   const float dval = a.dvec[(int64_t)head * a.Lp + my_q];
 
-  const int64_t kv_end = (q0 + QBM < a.L) ? q0 + QBM : a.L;
-  const int n_kt = (int)((kv_end + QBN - 1) / QBN);
+  const int kv_end = (q0 + QBM < L) ? q0 + QBM : L;
+  const int n_kt = (kv_end + QBN - 1) / QBN;
+
+  // per-lane element offsets, fixed for the whole loop
+  //  K/V rows (A operands of S^T and dP^T): row kb*32 + l32, chunk 2ks + g
+  int koff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = tile_off(l32, 2 * ks + g);
+  //  K^T (A operand of dQ^T, see tile_read_t): column block db, rows
+  //  4g + (lane%16)/4 and +8; 16 st more rows are an immediate
+  int offt[4][2];
+  {
+    const int sl = lane & 15, grp2 = (lane >> 4) & 1;
+    const int rr = 4 * g + (sl >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int col = db * 32 + 16 * grp2 + 4 * (sl & 3);
+      offt[db][0] = tile_off(rr, col >> 3) + (col & 7);
+      offt[db][1] = tile_off(rr + 8, col >> 3) + (col & 7);
+    }
+  }
+  //  tile copies: wave w moves rows 16w .. 16w+15 of the K and V tiles
+  uint32_t tdma[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * wave + 4 * i + (lane >> 4);
+    tdma[i] = (uint32_t)(row * 128 + (((lane & 15) ^ swz(row)) << 3));
+  }
+  auto load = [&](int kt, uint16_t* Kd, uint16_t* Vd) {
+    const uint16_t* ksrc = kp + (int64_t)kt * QBN * 128;
+    const uint16_t* vsrc = vp + (int64_t)kt * QBN * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dma16_untracked(ksrc + tdma[i], lds_addr(Kd + (wave * 4 + i) * 512));
+      dma16_untracked(vsrc + tdma[i], lds_addr(Vd + (wave * 4 + i) * 512));
+    }
+  };
 
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
   const float c = a.scale_log2;
 
-  // single-buffered K/V tiles: with two workgroups per CU the other
-  // workgroup's MFMAs cover this one's loads
-  for (int kt = 0; kt < n_kt; ++kt) {
-    {
-      TileCopy<QBN> pk, pv;
-      pk.load(kp + (int64_t)kt * QBN * 128, tid);
-      pv.load(vp + (int64_t)kt * QBN * 128, tid);
-      __syncthreads();  // previous tile's reads are done
-      pk.store(sm.K, tid);
-      pv.store(sm.V, tid);
-      __syncthreads();
-    }
-    const int64_t kstart = (int64_t)kt * QBN;
-    if (kstart <= r0 + 31) {
-      const bool need_mask = kstart + QBN - 1 > r0;
-      // S^T = K Q^T, dP^T = V dO^T: element (key kb*32+acc_row(r,g), query my_q)
-      f32x16 sv[2], dp[2];
+  auto step = [&](int kt, const uint16_t* Kt, const uint16_t* Vt) {
+    const int kstart = kt * QBN;
+    if (kstart > r0 + 31) return;  // every key of the tile is in this wave's future
+    // S^T = K Q^T, dP^T = V dO^T: element (key kb*32+acc_row(r,g), query my_q)
+    f32x16 sv[2], dp[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sv[kb] = f32x16{};
-        dp[kb] = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) {
+      sv[kb] = f32x16{};
+      dp[kb] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          sv[kb] = mfma32(tile_read_row(sm.K, kb * 32 + l32, 2 * ks + g), qreg[ks], sv[kb]);
-          dp[kb] = mfma32(tile_read_row(sm.V, kb * 32 + l32, 2 * ks + g), doreg[ks], dp[kb]);
-        }
-      }
-      u32x4 pS[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float ds[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], c, -lse2));
-          if (need_mask && kstart + kb * 32 + acc_row(r, g) > my_q) p = 0.f;
-          ds[r] = p * (dp[kb][r] - dval);
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            pS[kb * 2 + h][t] = pack_bf16x2(ds[8 * h + 2 * t], ds[8 * h + 2 * t + 1]);
-      }
-      // dQ^T += K^T dS^T; B slot t of step st is key 16*st + 8*(t/4) + 4*g + t%4
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[db] = mfma32(tile_read_t(sm.K, st * 16, db * 32, lane), pS[st], acc[db]);
+      for (int ks = 0; ks < 8; ++ks) {
+        sv[kb] = mfma32(*reinterpret_cast<const u32x4*>(Kt + koff[ks] + kb * 4096), qreg[ks], sv[kb]);
+        dp[kb] = mfma32(*reinterpret_cast<const u32x4*>(Vt + koff[ks] + kb * 4096), doreg[ks], dp[kb]);
       }
     }
+    if (kstart + QBN - 1 > r0) {  // the tile reaches past this wave's first query
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kstart + kb * 32 + acc_row(r, g) > my_q) sv[kb][r] = -__builtin_inff();
+    }
+    u32x4 pS[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], c, -lse2));
+        ds[r] = p * (dp[kb][r] - dval);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          pS[kb * 2 + h][t] = pack_bf16x2(ds[8 * h + 2 * t], ds[8 * h + 2 * t + 1]);
+    }
+    // dQ^T += K^T dS^T; B slot t of step st is key 16*st + 8*(t/4) + 4*g + t%4
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const u32x2 lo = lds_read_tr16(Kt + offt[db][0] + st * 2048);
+        const u32x2 hi = lds_read_tr16(Kt + offt[db][1] + st * 2048);
+        acc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pS[st], acc[db]);
+      }
+  };
+
+  load(0, sm.K0, sm.V0);
+  lds_dma_wait();
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    if (kt + 1 < n_kt) load(kt + 1, sm.K1, sm.V1);
+    step(kt, sm.K0, sm.V0);
+    lds_dma_wait();
+    __syncthreads();
+    if (kt + 1 >= n_kt) break;
+    if (kt + 2 < n_kt) load(kt + 2, sm.K0, sm.V0);
+    step(kt + 1, sm.K1, sm.V1);
+    lds_dma_wait();
+    __syncthreads();
   }
 
-  if (my_q >= a.L) return;
+  if (my_q >= L) return;
   // element (d = db*32 + acc_row(r,g), query my_q): scale, inverse RoPE, bf16
-  uint16_t* orow = a.dq_out + my_q * a.dq_ld + (int64_t)head * 128;
+  uint16_t* orow = a.dq_out + (int64_t)my_q * a.dq_ld + (int64_t)head * 128;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
