@@ -4,34 +4,37 @@
 //   NT  x . W_rows^T, O . W_o^T       (both operands k-contiguous)
 //   NN  dy . W_o[:, cols], dqkv . W   (B n-contiguous)
 //   TN  dy^T . O, dqkv^T . x          (both m/n-contiguous; K = L, split-K)
-// Workgroup tile 256 x 256 x 64 on 512 threads: 8 waves, two per SIMD, each
-// owning 128 x 64 of C as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (fp32
-// accumulators, 128 registers).  Operand tiles are staged in LDS as they lie
-// in memory -- no transposing stores:
-//  * a k-contiguous operand is [256 rows][64 k] with 128-byte rows and the
-//    16-byte chunk index XORed with (row / 2) % 8, so 16 lanes reading 16
+// Workgroup tile 256 x 256, k step 32, on 512 threads: 8 waves, two per
+// SIMD, each owning 128 x 64 of C as 4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 128 registers).
+// Operand tiles go straight from global memory to LDS by asynchronous
+// global->LDS copies, four k steps in flight (four LDS stages, 128 KB), so a
+// tile is requested three k steps before its MFMAs need it; the copies stage
+// the tiles as they lie in memory, no transposing stores:
+//  * a k-contiguous operand is [256 rows][32 k] with 64-byte rows and the
+//    16-byte chunk index XORed with (row / 4) % 4, so 16 lanes reading 16
 //    rows at one k offset hit 16 different bank groups;
-//  * an m/n-contiguous operand is [64 k][256] kept as two [64][128] halves in
+//  * an m/n-contiguous operand is [32 k][256] kept as two [32][128] halves in
 //    the swizzled 256-byte-row layout of common.h and read with the LDS
 //    transpose read (ds_read_b64_tr_b16), which hands each lane eight
 //    consecutive k of one column.
-// Global loads for k step t+1 are issued before the MFMAs of step t
-// (register double buffering, two LDS buffers, one barrier per step).
+// Rows past M or N are read clamped (their products land in rows or columns
+// of C that are not stored); k rows past the end of a split are zeroed in
+// LDS after they land, so clamped reads never reach a stored result.
 #include "kernels.h"
 
 namespace upipe {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int NT = 512;                     // threads
+constexpr int STAGES = 4;
 constexpr int TILE = 256 * BK;              // elements of one operand tile
-constexpr int HALF = 128 * BK;              // one [64][128] half of an m/n-major tile
+constexpr int HALF = 128 * BK;              // one [32][128] half of an m/n-major tile
+constexpr int STAGE = 2 * TILE;             // A and B tiles of one k step
 
 __device__ __forceinline__ int kmaj_off(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
-}
-__device__ __forceinline__ int mnmaj_off(int k, int chunk32) {
-  return (chunk32 >> 4) * HALF + tile_off(k, chunk32 & 15);
+  return row * BK + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
 
 __device__ __forceinline__ int64_t seg_map(const RowSegments& s, int idx) {
@@ -45,79 +48,113 @@ __device__ __forceinline__ int64_t seg_map(const RowSegments& s, int idx) {
   return s.row0[0] + idx;  // unreachable for valid maps
 }
 
+// s_waitcnt vmcnt(n), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 template <bool A_K, bool B_K, int EPI>
 __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // 128 KB
-  auto As = [&](int b) { return smem + 2 * b * TILE; };
-  auto Bs = [&](int b) { return smem + (2 * b + 1) * TILE; };
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * STAGE];  // 128 KB
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int g = lane >> 5, l32 = lane & 31;
 
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
-  const int kbeg = blockIdx.z * p.k_per_split;
+  // XCD-aware tile order: the dispatcher deals workgroups to the 8 XCDs
+  // round-robin, so workgroup i runs on XCD i % 8.  Renumber so that each
+  // XCD receives one contiguous range of tiles (n fastest): the workgroups
+  // an XCD runs together then share A row panels and B k-slices in its L2
+  // instead of every XCD fetching every panel.
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int total = gx * gy * gridDim.z;
+  const int id = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int q8 = total >> 3, r8 = total & 7, xcd = id & 7, local = id >> 3;
+  const int tile = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + local;
+  const int n0 = (tile % gx) * BN;
+  const int m0 = ((tile / gx) % gy) * BM;
+  const int kbeg = (tile / (gx * gy)) * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int nk = (kend - kbeg + BK - 1) / BK;
 
-  // ---- per-thread source pointers of the k-contiguous operands
-  const uint16_t* a_rows[4];
-  bool a_ok[4];
-  const uint16_t* b_rows[4];
-  bool b_ok[4];
+  // ---- copy plan: each wave moves blocks 2*wave, 2*wave+1 (1 KB each) of
+  // the A tile and of the B tile; per lane a source pointer (k = 0 of the
+  // split) and, for m/n-major operands, its k row within the tile
+  const uint16_t* asrc[2];
+  const uint16_t* bsrc[2];
+  int arow[2], brow[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + NT * i;
-    const int r = c >> 3, ch = c & 7;
-    if (A_K) {
-      const int m = m0 + r;
-      a_ok[i] = m < p.M;
-      a_rows[i] = p.A + (int64_t)(a_ok[i] ? m : 0) * p.lda + ch * 8;
+  for (int i = 0; i < 2; ++i) {
+    const int n = 2 * wave + i;
+    if (A_K) {  // 16 rows x 64 bytes per block
+      const int row = 16 * n + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int m = min(m0 + row, p.M - 1);
+      asrc[i] = p.A + (int64_t)m * p.lda + kbeg + c * 8;
+      arow[i] = 0;
+    } else {    // 4 k rows x 256 bytes of one 128-column half per block
+      const int half = n >> 3, row = 4 * (n & 7) + (lane >> 4);
+      const int c = (lane & 15) ^ swz(row);
+      const int col = min(m0 + half * 128 + c * 8, p.M - 8);
+      asrc[i] = p.A + (int64_t)kbeg * p.lda + col;
+      arow[i] = row;
     }
     if (B_K) {
-      const int n = n0 + r;
-      b_ok[i] = n < p.N;
-      b_rows[i] = p.B + seg_map(p.bseg, b_ok[i] ? n : 0) * p.ldb + ch * 8;
+      const int row = 16 * n + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int nn = min(n0 + row, p.N - 1);
+      bsrc[i] = p.B + seg_map(p.bseg, nn) * p.ldb + kbeg + c * 8;
+      brow[i] = 0;
+    } else {
+      const int half = n >> 3, row = 4 * (n & 7) + (lane >> 4);
+      const int c = (lane & 15) ^ swz(row);
+      const int col = min(n0 + half * 128 + c * 8, p.N - 8);
+      bsrc[i] = p.B + col;  // rows come from the segment map per k step
+      brow[i] = row;
     }
   }
-
-  u32x4 ra[4], rb[4];
-  auto load_tiles = [&](int kt) {
-    const int k0 = kbeg + kt * BK;
+  // issue the copies of k step kt into stage kt % STAGES
+  auto issue = [&](int kt) {
+    const int k0 = kt * BK;  // relative to kbeg
+    uint16_t* st = smem + (kt % STAGES) * STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + NT * i;
+    for (int i = 0; i < 2; ++i) {
+      const int n = 2 * wave + i;
+      const uint16_t* a;
       if (A_K) {
-        ra[i] = a_ok[i] ? *reinterpret_cast<const u32x4*>(a_rows[i] + k0) : u32x4{0, 0, 0, 0};
+        a = asrc[i] + k0;
       } else {
-        const int k = k0 + (c >> 5), col = m0 + (c & 31) * 8;
-        ra[i] = (k < kend && col < p.M)
-                    ? *reinterpret_cast<const u32x4*>(p.A + (int64_t)k * p.lda + col)
-                    : u32x4{0, 0, 0, 0};
+        const int k = min(kbeg + k0 + arow[i], kend - 1) - kbeg;
+        a = asrc[i] + (int64_t)k * p.lda;
       }
+      dma16_untracked(a, lds_addr(st + n * 512));
+      const uint16_t* b;
       if (B_K) {
-        rb[i] = b_ok[i] ? *reinterpret_cast<const u32x4*>(b_rows[i] + k0) : u32x4{0, 0, 0, 0};
+        b = bsrc[i] + k0;
       } else {
-        // a 64-row k tile never crosses a segment (segments are multiples of 128)
-        const int k = k0 + (c >> 5), col = n0 + (c & 31) * 8;
-        rb[i] = (k < kend && col < p.N)
-                    ? *reinterpret_cast<const u32x4*>(p.B + (seg_map(p.bseg, k0) + (c >> 5)) * p.ldb + col)
-                    : u32x4{0, 0, 0, 0};
+        // a 32-row k step never crosses a segment (segments are multiples of
+        // 128): one uniform segment lookup per step, rows clamped only in a
+        // split's last, partial step
+        const int kb0 = kbeg + k0;
+        const int64_t row = kb0 + BK <= kend ? seg_map(p.bseg, kb0) + brow[i]
+                                             : seg_map(p.bseg, min(kb0 + brow[i], kend - 1));
+        b = bsrc[i] + row * p.ldb;
       }
+      dma16_untracked(b, lds_addr(st + TILE + n * 512));
     }
   };
-  auto store_tiles = [&](int buf) {
+
+  // per-lane LDS element offsets of the MFMA operands within a stage
+  int aoff[2], boff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + NT * i;
-      const int aofs = A_K ? kmaj_off(c >> 3, c & 7) : mnmaj_off(c >> 5, c & 31);
-      *reinterpret_cast<u32x4*>(As(buf) + aofs) = ra[i];
-      const int bofs = B_K ? kmaj_off(c >> 3, c & 7) : mnmaj_off(c >> 5, c & 31);
-      *reinterpret_cast<u32x4*>(Bs(buf) + bofs) = rb[i];
-    }
-  };
+  for (int ks = 0; ks < 2; ++ks) {
+    aoff[ks] = A_K ? kmaj_off(wm * 128 + l32, 2 * ks + g) : 0;
+    boff[ks] = B_K ? kmaj_off(wn * 64 + l32, 2 * ks + g) : 0;
+  }
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -125,24 +162,41 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  if (nk > 0) {
-    load_tiles(0);
-    store_tiles(0);
-  }
-  __syncthreads();
+  // prologue: three k steps in flight
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t)
+    if (t < nk) issue(t);
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tiles(kt + 1);
-    const uint16_t* at = As(cur);
-    const uint16_t* bt = Bs(cur);
+    // this wave's copies of step kt are done once at most the copies of the
+    // (up to two) later steps already issued are outstanding
+    const int later = min(nk - 1 - kt, STAGES - 2);
+    if (later >= 2) wait_vmcnt<8>();
+    else if (later == 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's copies of step kt landed; step kt-1 fully read
+    const int k0 = kbeg + kt * BK;
+    uint16_t* st = smem + (kt % STAGES) * STAGE;
+    if (!A_K && k0 + BK > kend) {
+      // k rows past the end of the split were read clamped: zero them in A
+      const int valid = kend - k0;
+      for (int c = tid; c < BK * 32; c += NT) {
+        const int row = c >> 5;
+        if (row >= valid)
+          *reinterpret_cast<u32x4*>(st + (c & 16 ? HALF : 0) + row * 128 + (c & 15) * 8) = u32x4{0, 0, 0, 0};
+      }
+      __syncthreads();
+    }
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);  // into the stage read at kt-1
+    const uint16_t* at = st;
+    const uint16_t* bt = st + TILE;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       u32x4 a[4], b[2];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const int row = wm * 128 + mb * 32;
         if (A_K)
-          a[mb] = *reinterpret_cast<const u32x4*>(at + kmaj_off(row + l32, 2 * ks + g));
+          a[mb] = *reinterpret_cast<const u32x4*>(at + aoff[ks] + mb * 32 * BK);
         else
           a[mb] = tile_read_t_nat(at + wm * HALF, ks * 16, mb * 32, lane);
       }
@@ -150,7 +204,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
       for (int nb = 0; nb < 2; ++nb) {
         const int col = wn * 64 + nb * 32;
         if (B_K)
-          b[nb] = *reinterpret_cast<const u32x4*>(bt + kmaj_off(col + l32, 2 * ks + g));
+          b[nb] = *reinterpret_cast<const u32x4*>(bt + boff[ks] + nb * 32 * BK);
         else
           b[nb] = tile_read_t_nat(bt + (col >> 7) * HALF, ks * 16, col & 127, lane);
       }
@@ -159,9 +213,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[mb], b[nb], acc[mb][nb]);
     }
-    if (kt + 1 < nk) store_tiles(cur ^ 1);
-    __syncthreads();
   }
+  __syncthreads();  // the epilogue reuses the stages
 
   if (EPI == EPI_ATOMIC_F32) {
     // split-K: every split adds its partial tile into one fp32 accumulator
@@ -186,6 +239,19 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    // accumulate: the old values of this half's C rows are requested first,
+    // all eight at once, so their latency overlaps the LDS staging below
+    u32x4 old[8];
+    if (EPI == EPI_ACCUM_BF16) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int c = tid + NT * it;
+        const int m = m0 + half * 128 + (c >> 5), n = n0 + (c & 31) * 8;
+        old[it] = (m < p.M && n < p.N)
+                      ? *reinterpret_cast<const u32x4*>(C + (int64_t)m * p.ldc + n)
+                      : u32x4{0, 0, 0, 0};
+      }
+    }
     if (wm == half) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
@@ -223,11 +289,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
           hi = f32x4{v[4], v[5], v[6], v[7]};
         }
         if (EPI == EPI_ACCUM_BF16) {
-          u32x4 old = *dst;
-          lo[0] += bf16_lo(old[0]); lo[1] += bf16_hi(old[0]);
-          lo[2] += bf16_lo(old[1]); lo[3] += bf16_hi(old[1]);
-          hi[0] += bf16_lo(old[2]); hi[1] += bf16_hi(old[2]);
-          hi[2] += bf16_lo(old[3]); hi[3] += bf16_hi(old[3]);
+          const u32x4 o = old[it];
+          lo[0] += bf16_lo(o[0]); lo[1] += bf16_hi(o[0]);
+          lo[2] += bf16_lo(o[1]); lo[3] += bf16_hi(o[1]);
+          hi[0] += bf16_lo(o[2]); hi[1] += bf16_hi(o[2]);
+          hi[2] += bf16_lo(o[3]); hi[3] += bf16_hi(o[3]);
         }
         u32x4 out;
         if (EPI == EPI_STORE_BF16 && p.f16_from > 0 && n >= p.f16_from) {
