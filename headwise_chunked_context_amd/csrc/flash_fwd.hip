@@ -99,15 +99,18 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     kdma[i] = (uint32_t)(row * 128 + (((lane & 15) ^ swz(row)) << 3));
   }
 
-  // tile kt -> LDS: K rows kt*64.. (swizzled on the way), V^T tile kt as is
-  auto dma = [&](int kt, uint16_t* Kd, uint16_t* Vd) {
-    const uint16_t* ks = kp + (int64_t)kt * BN * 128;
-    const uint16_t* vs = vp + (int64_t)kt * BN * 128 + wave * 2048 + lane * 8;
+  // K tile kt -> LDS (swizzled on the way); V^T tile kt -> LDS as is
+  auto dma_k = [&](int kt, uint16_t* Kd) {
+    const uint16_t* src = kp + (int64_t)kt * BN * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds(ks + kdma[i], (lds_void*)(Kd + (wave * 4 + i) * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vs + i * 512, (lds_void*)(Vd + (wave * 4 + i) * 512), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(src + kdma[i], (lds_void*)(Kd + (wave * 4 + i) * 512), 16, 0, 0);
+  };
+  auto dma_v = [&](int kt, uint16_t* Vd) {
+    const uint16_t* src = vp + (int64_t)kt * BN * 128 + wave * 2048 + lane * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(src + i * 512, (lds_void*)(Vd + (wave * 4 + i) * 512), 16, 0, 0);
   };
 
   f32x16 acc_o[4];
@@ -118,10 +121,8 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   const float c = a.scale_log2;
   const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 
-  auto step = [&](int kt, const uint16_t* Kc, const uint16_t* Vc) {
-    const int kstart = kt * BN;
-    if (kstart > r0 + 31) return;  // every key of the tile is in this wave's future
-    f32x16 s[2];
+  // S^T of one key tile: element (key kb*32 + acc_row(r,g), query my_q)
+  auto scores = [&](const uint16_t* Kc, f32x16* s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
@@ -129,22 +130,36 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
       for (int ks = 0; ks < 8; ++ks)
         s[kb] = mfma32(*reinterpret_cast<const u32x4*>(Kc + koff[ks] + kb * 4096), qreg[ks], s[kb]);
     }
-    if (kstart + BN - 1 > r0) {  // the tile reaches past this wave's first query
+  };
+
+  // Software pipeline over key tiles: iteration t holds the scores of tile
+  // t (computed one iteration earlier) and, in one straight-line block,
+  // issues the score MFMAs of tile t+1 alongside the softmax VALU work of
+  // tile t and then its O^T += V^T P^T MFMAs, so matrix and vector units
+  // work at the same time within a wave.  K and V^T have their own buffer
+  // pairs: during iteration t the K buffer holds tile t+1 and the V^T
+  // buffer tile t, while the copies of K tile t+2 and V^T tile t+1 fill the
+  // other two.
+  f32x16 sc[2];
+  auto iteration = [&](int kt, const uint16_t* Knext, const uint16_t* Vc) {
+    const int kstart = kt * BN;
+    if (kstart > r0 + 31) return;  // this and every later tile lie in the wave's future
+    if (kstart + BN - 1 > r0) {    // the tile reaches past this wave's first query
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kstart + kb * 32 + acc_row(r, g) > my_q) s[kb][r] = -__builtin_inff();
+          if (kstart + kb * 32 + acc_row(r, g) > my_q) sc[kb][r] = -__builtin_inff();
     }
     // running maximum, raised lazily: only when some row's new score
     // exceeds it by more than 2^8 in the exponent (wave-uniform), so the
     // 64-register rescale of O runs a few times per row instead of every
     // tile; in between P <= 256, well inside fp16 and fp32
-    float mx = fmaxf(s[0][0], s[0][1]);
+    float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[0][r]), s[0][r + 1]);
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[0][r]), sc[0][r + 1]);
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[1][r]), s[1][r + 1]);
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[1][r]), sc[1][r + 1]);
     mx = half_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx * c > fmaf(m_run, c, 8.f))) {
       const float m_new = fmaxf(m_run, mx);
@@ -155,20 +170,24 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
       m_run = m_new;
     }
     const float mc = m_run * c;
+    // scores of the next tile (unused past the last tile or the diagonal;
+    // the buffer then holds stale but finite-or-ignored data)
+    f32x16 sn[2];
+    scores(Knext, sn);
     // P in fp16, packed in pairs as the B operand; the row sum is taken
     // from each fp16 pair before it goes into the operand vector
     u32x4 pb[4];
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      float p[16];
+      float pr[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mc));
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -mc));
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const f32x2 pair = {p[8 * h + 2 * t], p[8 * h + 2 * t + 1]};
+          const f32x2 pair = {pr[8 * h + 2 * t], pr[8 * h + 2 * t + 1]};
           const f16x2 hp = __builtin_convertvector(pair, f16x2);
           if (t & 1)
             ls1 = __builtin_amdgcn_fdot2(hp, ones, ls1, false);
@@ -185,19 +204,29 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
         acc_o[db] = mfma32_f16(*reinterpret_cast<const u32x4*>(Vc + voff[st] + db * 2048), pb[st], acc_o[db]);
+    sc[0] = sn[0];
+    sc[1] = sn[1];
   };
 
-  dma(0, K0, V0);
+  dma_k(0, K0);
+  dma_v(0, V0);
+  if (n_kt > 1) dma_k(1, K1);
   lds_dma_wait();
   __syncthreads();
+  scores(K0, sc);   // tile 0 is visible to every wave
+  __syncthreads();  // K0 is refilled below
   for (int kt = 0; kt < n_kt; kt += 2) {
-    if (kt + 1 < n_kt) dma(kt + 1, K1, V1);
-    step(kt, K0, V0);
+    // K1 = tile kt+1, V0 = tile kt
+    if (kt + 2 < n_kt) dma_k(kt + 2, K0);
+    if (kt + 1 < n_kt) dma_v(kt + 1, V1);
+    iteration(kt, K1, V0);
     lds_dma_wait();
     __syncthreads();
     if (kt + 1 >= n_kt) break;
-    if (kt + 2 < n_kt) dma(kt + 2, K0, V0);
-    step(kt + 1, K1, V1);
+    // K0 = tile kt+2, V1 = tile kt+1
+    if (kt + 3 < n_kt) dma_k(kt + 3, K1);
+    if (kt + 2 < n_kt) dma_v(kt + 2, V0);
+    iteration(kt + 1, K0, V1);
     lds_dma_wait();
     __syncthreads();
   }
