@@ -176,6 +176,12 @@ __device__ __forceinline__ void dma4_untracked(const void* src, uint32_t lds_dst
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+// 16-byte LDS read at byte address addr + off (off a compile-time constant
+// that folds into the instruction's offset field)
+__device__ __forceinline__ u32x4 lds_load16(uint32_t addr, uint32_t off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+      (uintptr_t)(addr + off));
+}
 // LDS byte address of a pointer into a __shared__ array
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

@@ -177,16 +177,15 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
     // S = Q K^T and dP = dO V^T: element (query 32*qh + acc_row(r,g), key my_key)
     f32x16 sv = f32x16{}, dp = f32x16{};
     // K/V addresses are rebuilt every step (8 adds) rather than held in 8
-    // more registers
-    int dko = dko_init;
-    asm volatile("" : "+s"(dko));
+    // more registers; V follows K directly, so its address is the K
+    // address plus an immediate
+    uint32_t kb = lds_addr(Ks) + 2 * dko_init;
+    asm volatile("" : "+s"(kb));
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const int ok = offq[ks] + dko;
-      sv = mfma32(*reinterpret_cast<const u32x4*>(Qt + offq[ks]),
-                  *reinterpret_cast<const u32x4*>(Ks + ok), sv);
-      dp = mfma32(*reinterpret_cast<const u32x4*>(Ot + offq[ks]),
-                  *reinterpret_cast<const u32x4*>(Vs + ok), dp);
+      const uint32_t ka = kb + 2 * offq[ks];
+      sv = mfma32(*reinterpret_cast<const u32x4*>(Qt + offq[ks]), lds_load16(ka, 0), sv);
+      dp = mfma32(*reinterpret_cast<const u32x4*>(Ot + offq[ks]), lds_load16(ka, BNK * 128 * 2), dp);
     }
     if (need_mask) {  // key after the query, or a padding query row
 #pragma unroll
