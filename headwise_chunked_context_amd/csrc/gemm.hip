@@ -6,7 +6,9 @@
 //   TN  dy^T . O, dqkv^T . x          (both m/n-contiguous; K = L, split-K)
 // Workgroup tile 256 x 256, k step 32, on 512 threads: 8 waves, two per
 // SIMD, each owning 128 x 64 of C as 4 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 128 registers).
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 128 registers).  (One wave
+// per SIMD with 128 x 128 each halves the LDS reads per MFMA but measured
+// 10-15% slower: a single wave cannot hide the LDS and copy latencies.)
 // Operand tiles go straight from global memory to LDS by asynchronous
 // global->LDS copies, four k steps in flight (four LDS stages, 128 KB), so a
 // tile is requested three k steps before its MFMAs need it; the copies stage
@@ -27,8 +29,12 @@ namespace upipe {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int NT = 512;                     // threads
+constexpr int WM = 2, WN = 4;               // waves along M and N
+constexpr int NT = 64 * WM * WN;            // threads
+constexpr int MB = BM / WM / 32;            // 32x32 blocks per wave along M
+constexpr int NB = BN / WN / 32;            // ... along N
 constexpr int STAGES = 4;
+static_assert(WM == 2, "the bf16 epilogue stages one 128-row half of C per wave row");
 constexpr int TILE = 256 * BK;              // elements of one operand tile
 constexpr int HALF = 128 * BK;              // one [32][128] half of an m/n-major tile
 constexpr int STAGE = 2 * TILE;             // A and B tiles of one k step
@@ -62,7 +68,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WN, wn = wave % WN;
   const int g = lane >> 5, l32 = lane & 31;
 
   // XCD-aware tile order: the dispatcher deals workgroups to the 8 XCDs
@@ -81,15 +87,16 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int nk = (kend - kbeg + BK - 1) / BK;
 
-  // ---- copy plan: each wave moves blocks 2*wave, 2*wave+1 (1 KB each) of
+  // ---- copy plan: each wave moves CPW consecutive 1 KB blocks of
   // the A tile and of the B tile; per lane a source pointer (k = 0 of the
   // split) and, for m/n-major operands, its k row within the tile
-  const uint16_t* asrc[2];
-  const uint16_t* bsrc[2];
-  int arow[2], brow[2];
+  constexpr int CPW = 16 / (WM * WN);  // 16 blocks of 1 KB per operand tile
+  const uint16_t* asrc[CPW];
+  const uint16_t* bsrc[CPW];
+  int arow[CPW], brow[CPW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int n = 2 * wave + i;
+  for (int i = 0; i < CPW; ++i) {
+    const int n = CPW * wave + i;
     if (A_K) {  // 16 rows x 64 bytes per block
       const int row = 16 * n + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 2) & 3);
@@ -122,8 +129,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     const int k0 = kt * BK;  // relative to kbeg
     uint16_t* st = smem + (kt % STAGES) * STAGE;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int n = 2 * wave + i;
+    for (int i = 0; i < CPW; ++i) {
+      const int n = CPW * wave + i;
       const uint16_t* a;
       if (A_K) {
         a = asrc[i] + k0;
@@ -152,15 +159,15 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   int aoff[2], boff[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    aoff[ks] = A_K ? kmaj_off(wm * 128 + l32, 2 * ks + g) : 0;
-    boff[ks] = B_K ? kmaj_off(wn * 64 + l32, 2 * ks + g) : 0;
+    aoff[ks] = A_K ? kmaj_off(wm * (BM / WM) + l32, 2 * ks + g) : 0;
+    boff[ks] = B_K ? kmaj_off(wn * (BN / WN) + l32, 2 * ks + g) : 0;
   }
 
-  f32x16 acc[4][2];
+  f32x16 acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
   // prologue: three k steps in flight
 #pragma unroll
@@ -192,26 +199,26 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     const uint16_t* bt = st + TILE;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4 a[4], b[2];
+      u32x4 a[MB], b[NB];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
         if (A_K)
           a[mb] = *reinterpret_cast<const u32x4*>(at + aoff[ks] + mb * 32 * BK);
         else
           a[mb] = tile_read_t_nat(at + wm * HALF, ks * 16, mb * 32, lane);
       }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = wn * 64 + nb * 32;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = wn * (BN / WN) + nb * 32;
         if (B_K)
           b[nb] = *reinterpret_cast<const u32x4*>(bt + boff[ks] + nb * 32 * BK);
         else
           b[nb] = tile_read_t_nat(bt + (col >> 7) * HALF, ks * 16, col & 127, lane);
       }
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[mb], b[nb], acc[mb][nb]);
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(a[mb], b[nb], acc[mb][nb]);
     }
   }
   __syncthreads();  // the epilogue reuses the stages
@@ -220,13 +227,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     // split-K: every split adds its partial tile into one fp32 accumulator
     float* C = reinterpret_cast<float*>(p.C);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int n = n0 + wn * 64 + nb * 32 + l32;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int n = n0 + wn * (BN / WN) + nb * 32 + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * 128 + mb * 32 + acc_row(r, g);
+          const int m = m0 + wm * (BM / WM) + mb * 32 + acc_row(r, g);
           if (m < p.M && n < p.N) atomicAdd(C + (int64_t)m * p.N + n, acc[mb][nb][r]);
         }
       }
@@ -241,10 +248,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   for (int half = 0; half < 2; ++half) {
     // accumulate: the old values of this half's C rows are requested first,
     // all eight at once, so their latency overlaps the LDS staging below
-    u32x4 old[8];
+    constexpr int EIT = 128 * (BN / 8) / NT;  // 16-byte chunks per thread per half
+    u32x4 old[EIT];
     if (EPI == EPI_ACCUM_BF16) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
+      for (int it = 0; it < EIT; ++it) {
         const int c = tid + NT * it;
         const int m = m0 + half * 128 + (c >> 5), n = n0 + (c & 31) * 8;
         old[it] = (m < p.M && n < p.N)
@@ -254,16 +262,16 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     }
     if (wm == half) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            Cs[(mb * 32 + acc_row(r, g)) * BN + wn * 64 + nb * 32 + l32] = acc[mb][nb][r];
+            Cs[(mb * 32 + acc_row(r, g)) * BN + wn * (BN / WN) + nb * 32 + l32] = acc[mb][nb][r];
     }
     __syncthreads();
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
+    for (int it = 0; it < EIT; ++it) {
       const int c = tid + NT * it;
       const int r = c >> 5, cc = c & 31;
       const int m = m0 + half * 128 + r;
