@@ -212,6 +212,9 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
       pS[r4 >> 1][2 * (r4 & 1)] = pack_bf16x2(dsv[0], dsv[1]);
       pS[r4 >> 1][2 * (r4 & 1) + 1] = pack_bf16x2(dsv[2], dsv[3]);
     }
+    // the dV/dK MFMAs issue at raised wave priority (the other wave of the
+    // SIMD then gets the VALU slots for its P/dS work)
+    __builtin_amdgcn_s_setprio(1);
     // dV^T += dO^T P, dK^T += Q^T dS over this wave's 32 queries; B slot t
     // of step h is query 32*qh + 16*h + 8*(t/4) + 4*g + t%4
 #pragma unroll
@@ -225,6 +228,7 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
         const u32x2 q_hi = lds_read_tr16(Qt + offt[db][1] + h * 2048);
         acc_dk[db] = mfma32(u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}, pS[h], acc_dk[db]);
       }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   if (nsteps > 0) load_next(Q0, O0, L0, E0);
@@ -408,6 +412,9 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
     if (kstart > r0 + 31) return;  // every key of the tile is in this wave's future
     // S^T = K Q^T, dP^T = V dO^T: element (key kb*32+acc_row(r,g), query my_q)
     f32x16 sv[2], dp[2];
+    // the S/dP MFMAs issue at raised wave priority, the rest at the default
+    // (measured: the dQ MFMAs at raised priority too is slower)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sv[kb] = f32x16{};
@@ -418,6 +425,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
         dp[kb] = mfma32(*reinterpret_cast<const u32x4*>(Vt + koff[ks] + kb * 4096), doreg[ks], dp[kb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (kstart + QBN - 1 > r0) {  // the tile reaches past this wave's first query
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
