@@ -56,17 +56,28 @@ int check_shape(int64_t L, int32_t hidden, int32_t n_q, int32_t n_kv, int32_t he
   return UPIPE_OK;
 }
 
-// Split-K factor of the weight-gradient GEMMs (reduction over L): enough
-// 256 x 256 workgroups to cover the 256 CUs twice, each split at least 512
-// rows of the sequence.
+// Split-K factor of the weight-gradient GEMMs (reduction over L).  The
+// 256 x 256 workgroups run one per CU, so the time of a split count s is
+// about ceil(tiles*s / 256) rounds of 1/s of the reduction each, plus a
+// small cost per split for the fp32 atomics of its epilogue (0.01 of the
+// unsplit time per split, fitted to measurements of the layer's two shapes).
+// Each split keeps at least 512 rows of the sequence.
 int dw_splits(int64_t L, int M, int N) {
-  int tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  int s = (512 + tiles - 1) / tiles;
-  int max_by_len = (int)((L + 511) / 512);
-  if (s > max_by_len) s = max_by_len;
-  if (s > 32) s = 32;
-  if (s < 1) s = 1;
-  return s;
+  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  int max_s = (int)((L + 511) / 512);
+  if (max_s > 32) max_s = 32;
+  if (max_s < 1) max_s = 1;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sp = 1; sp <= max_s; ++sp) {
+    const double rounds = (double)((tiles * sp + 255) / 256);
+    const double cost = rounds / sp + 0.01 * sp;
+    if (cost < best_cost - 1e-12) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
 }
 int k_per_split(int64_t L, int splits) {
   int64_t k = (L + splits - 1) / splits;
