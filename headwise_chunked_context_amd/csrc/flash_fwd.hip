@@ -46,8 +46,6 @@ namespace {
 constexpr int BM = 128;       // queries per workgroup
 constexpr int BN = 64;        // keys per step
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t K0[BN * 128];
   __shared__ __attribute__((aligned(16))) uint16_t K1[BN * 128];
@@ -103,14 +101,12 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   auto dma_k = [&](int kt, uint16_t* Kd) {
     const uint16_t* src = kp + (int64_t)kt * BN * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(src + kdma[i], (lds_void*)(Kd + (wave * 4 + i) * 512), 16, 0, 0);
+    for (int i = 0; i < 4; ++i) dma16_untracked(src + kdma[i], lds_addr(Kd + (wave * 4 + i) * 512));
   };
   auto dma_v = [&](int kt, uint16_t* Vd) {
     const uint16_t* src = vp + (int64_t)kt * BN * 128 + wave * 2048 + lane * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(src + i * 512, (lds_void*)(Vd + (wave * 4 + i) * 512), 16, 0, 0);
+    for (int i = 0; i < 4; ++i) dma16_untracked(src + i * 512, lds_addr(Vd + (wave * 4 + i) * 512));
   };
 
   f32x16 acc_o[4];
