@@ -108,59 +108,19 @@ __device__ __forceinline__ u32x4 tile_read_row(const uint16_t* tile, int row, in
   return *reinterpret_cast<const u32x4*>(tile + tile_off(row, chunk));
 }
 
-// Cooperative global -> LDS copy of `rows` x 128 elements (rows * 16 chunks),
-// 256 threads, into the swizzled layout; src rows are 128 elements apart.
-template <int ROWS>
-struct TileCopy {
-  static constexpr int N = ROWS * 16 / 256;
-  u32x4 v[N];
-  __device__ __forceinline__ void load(const uint16_t* src, int tid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      int c = tid + 256 * i;
-      v[i] = *reinterpret_cast<const u32x4*>(src + (c >> 4) * 128 + (c & 15) * 8);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      int c = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(tile + tile_off(c >> 4, c & 15)) = v[i];
-    }
-  }
-};
-
-// Asynchronous global -> LDS copy (global_load_lds_dwordx4) of ROWS x 128
-// elements, rows 128 elements apart in global memory, into the swizzled
-// tile layout.  NWAVES waves split the work; each wave instruction moves
-// 64 x 16 bytes into 1 KB of consecutive LDS, so lane i fetches the global
-// chunk that the swizzle places at that position.  The caller waits with
-// lds_dma_wait() and a barrier before reading the tile.
-template <int ROWS, int NWAVES>
-__device__ __forceinline__ void tile_dma(uint16_t* tile, const uint16_t* src, int wave, int lane) {
-  constexpr int PER_WAVE = ROWS * 16 / 64 / NWAVES;
-  static_assert(PER_WAVE * 64 * NWAVES == ROWS * 16, "tile must split evenly over the waves");
-#pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int n = wave * PER_WAVE + i;
-    const int q = n * 64 + lane;
-    const int row = q >> 4, chunk = (q & 15) ^ swz(q >> 4);
-    __builtin_amdgcn_global_load_lds(src + row * 128 + chunk * 8,
-                                     (__attribute__((address_space(3))) void*)(tile + n * 512),
-                                     16, 0, 0);
-  }
-}
-// The same copy issued as inline asm (16 or 4 bytes per lane; M0 = LDS
-// destination of lane 0).  The compiler then does not know that a copy into
-// LDS is in flight, so it does not make later LDS reads wait for it: it
-// cannot tell the two buffers of a double-buffered loop apart for every read
-// form (transpose reads in particular) and would otherwise wait for the
-// copy into the other buffer before each of them.  The caller owns
-// completion: lds_dma_wait() and a barrier before the destination is read,
-// and no copy into a buffer until every wave has passed the barrier that
-// follows its last read.  M0 is listed as clobbered; the compiler keeps no
-// value in it across other code (it sets M0 right before each of its own
-// uses), which the warning about clobbering a reserved register concerns.
+// Asynchronous global -> LDS copy (global_load_lds_dwordx4 / _dword): each
+// lane fetches 16 (or 4) bytes and the wave's data lands in consecutive LDS
+// from the address in M0 (lane i at M0 + 16i).  Issued as inline asm, so the
+// compiler does not know that a copy into LDS is in flight and does not
+// make later LDS reads wait for it: it cannot tell the two buffers of a
+// double-buffered loop apart for every read form (transpose reads in
+// particular) and would otherwise wait for the copy into the other buffer
+// before each of them.  The caller owns completion: lds_dma_wait() and a
+// barrier before the destination is read, and no copy into a buffer until
+// every wave has passed the barrier that follows its last read.  M0 is
+// listed as clobbered; the compiler keeps no value in it across other code
+// (it sets M0 right before each of its own uses), which the warning about
+// clobbering a reserved register concerns.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16_untracked(const void* src, uint32_t lds_dst) {
@@ -187,11 +147,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// 64 consecutive floats by one wave (global_load_lds_dword)
-__device__ __forceinline__ void vec64_dma(float* dst, const float* src, int lane) {
-  __builtin_amdgcn_global_load_lds(src + lane, (__attribute__((address_space(3))) void*)dst, 4, 0,
-                                   0);
-}
 // wait for this wave's outstanding vector-memory operations (vmcnt = 0)
 __device__ __forceinline__ void lds_dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
