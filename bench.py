@@ -138,6 +138,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, help="workload id in synthetic.WORKLOADS")
     ap.add_argument("--chunk", type=int, default=0, help="override the head chunk")
     ap.add_argument("--seq-len", type=int, default=0, help="override L (not a metric run)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="backward without the saved attention output (recomputed per chunk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -176,13 +178,15 @@ def main() -> int:
     del inp
     hidden = w.hidden
     ws_f = lib.workspace_bytes(w.L, hidden, w.n_q, w.n_kv, w.head_dim, hc, lib.PASS_FWD)
-    ws_b = lib.workspace_bytes(w.L, hidden, w.n_q, w.n_kv, w.head_dim, hc, lib.PASS_BWD)
+    bwd_pass = lib.PASS_BWD_RECOMPUTE if args.recompute else lib.PASS_BWD
+    ws_b = lib.workspace_bytes(w.L, hidden, w.n_q, w.n_kv, w.head_dim, hc, bwd_pass)
     # one workspace, sized for the larger pass, reused by every call
     ws = torch.empty(max(ws_f, ws_b), dtype=torch.uint8, device=dev)
 
     def step():
         _, o, lse = lib.attn_fwd(x, wq, wo, w.n_q, w.n_kv, hc, w.theta, workspace=ws)
-        lib.attn_bwd(x, wq, wo, o, lse, dy, w.n_q, w.n_kv, hc, w.theta, workspace=ws)
+        lib.attn_bwd(x, wq, wo, None if args.recompute else o, lse, dy, w.n_q, w.n_kv, hc, w.theta,
+                     workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -251,7 +255,7 @@ def main() -> int:
     chunks = [c for c in range(1, w.n_q + 1)
               if w.n_q % c == 0 and (c % (w.n_q // w.n_kv) == 0 or (w.n_q // w.n_kv) % c == 0)]
     ws_vs_chunk = {str(c): round(lib.workspace_bytes(w.L, hidden, w.n_q, w.n_kv, d, c,
-                                                     lib.PASS_BWD) / 2**30, 4) for c in chunks}
+                                                     bwd_pass) / 2**30, 4) for c in chunks}
 
     out = {
         "metric": "chunked causal attn fwd+bwd TFLOP/s at 1 GPU; peak workspace GiB vs chunk",
@@ -278,6 +282,7 @@ def main() -> int:
             "batch": 1,
             "causal": True,
             "parallelism": "single GPU (one GPU's share; no collectives)",
+            "backward": "recompute attention output" if args.recompute else "saved attention output",
         },
         "model_flops_per_step": flops,
         "roofline": roofline,

@@ -7,6 +7,7 @@ from .binding import (  # noqa: F401
     EXPORTS,
     KERNEL_KINDS,
     PASS_BWD,
+    PASS_BWD_RECOMPUTE,
     PASS_FWD,
     UPIPE_ECHUNK,
     UPIPE_EHIP,

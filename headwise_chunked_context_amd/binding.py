@@ -21,6 +21,7 @@ UPIPE_EWORKSPACE = -4
 UPIPE_EHIP = -5
 PASS_FWD = 0
 PASS_BWD = 1
+PASS_BWD_RECOMPUTE = 2
 
 # names declared in include/upipe_attn.h
 EXPORTS = (
@@ -159,7 +160,8 @@ def attn_fwd(x, w_qkv, w_o, n_q: int, n_kv: int, head_chunk: int, theta: float,
 def attn_bwd(x, w_qkv, w_o, o_saved, lse, dy, n_q: int, n_kv: int, head_chunk: int,
              theta: float, head_dim: int = 128, workspace=None, stream=None):
     """Backward of the chunked layer.  Returns (dx, dw_qkv, dw_o); in q/k/v-given
-    mode dx is dqkv and the weight gradients are None."""
+    mode dx is dqkv and the weight gradients are None.  With o_saved=None
+    (projection mode only) each chunk's attention output is recomputed."""
     import torch
 
     L = x.shape[0]
@@ -169,7 +171,8 @@ def attn_bwd(x, w_qkv, w_o, o_saved, lse, dy, n_q: int, n_kv: int, head_chunk: i
     dx = torch.empty_like(x)
     dw_qkv = torch.empty_like(w_qkv) if proj else None
     dw_o = torch.empty_like(w_o) if proj else None
-    ws_n = workspace_bytes(L, hidden, n_q, n_kv, head_dim, head_chunk, PASS_BWD)
+    pass_ = PASS_BWD if o_saved is not None else PASS_BWD_RECOMPUTE
+    ws_n = workspace_bytes(L, hidden, n_q, n_kv, head_dim, head_chunk, pass_)
     ws = _workspace(ws_n, dev, workspace)
     rc = lib().upipe_attn_bwd(L, hidden, n_q, n_kv, head_dim, float(theta), head_chunk,
                               _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(o_saved), _ptr(lse), _ptr(dy),

@@ -95,6 +95,8 @@ struct Plan {
   size_t lse2, dvec;           // [hc][Lp] fp32 (bwd)
   size_t dk_acc, dv_acc;       // [kc][Lp][d] fp32 (bwd, only when a group spans chunks)
   size_t dw_acc;               // fp32 weight-gradient accumulator (bwd, projection mode)
+  size_t o_c;                  // [L][hc d] bf16 recomputed attention output (bwd recompute)
+  size_t v_t;                  // [kc][Lp][d] fp16 transposed V tiles (bwd recompute)
   size_t total;
 };
 
@@ -115,7 +117,8 @@ Plan make_plan(const Shape& s, int pass) {
   p.q_rm = take(hc * head_bf16);
   p.k_rm = take(kc * head_bf16);
   p.v_rm = take(kc * head_bf16);
-  if (pass == UPIPE_PASS_BWD) {
+  p.o_c = p.v_t = no;
+  if (pass == UPIPE_PASS_BWD || pass == UPIPE_PASS_BWD_RECOMPUTE) {
     p.do_rm = take(hc * head_bf16);
     p.lse2 = take(hc * Lp * 4);
     p.dvec = take(hc * Lp * 4);
@@ -126,6 +129,13 @@ Plan make_plan(const Shape& s, int pass) {
     // fp32 split-K accumulator of the weight gradients: dW_o[:, cols(c)] is
     // [D][hc d], dW_qkv[rows(c)] is [(hc+2kc) d][D]
     p.dw_acc = s.proj ? take(width * (size_t)s.D * 4) : no;
+    if (pass == UPIPE_PASS_BWD_RECOMPUTE) {
+      // the chunk's attention output, recomputed (its LSE goes to lse2,
+      // which prep_dout rewrites afterwards), and the forward's V tiles,
+      // which persist while a KV group spans chunks
+      p.o_c = take((size_t)s.L * hc * d * 2);
+      p.v_t = take(kc * head_bf16);
+    }
   } else {
     p.do_rm = p.lse2 = p.dvec = p.dk_acc = p.dv_acc = p.dw_acc = no;
   }
@@ -297,10 +307,11 @@ const char* upipe_strerror(int status) {
 int upipe_attn_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t n_q_heads,
                                int32_t n_kv_heads, int32_t head_dim, int32_t head_chunk,
                                int32_t pass, size_t* bytes) {
-  if (!bytes || (pass != UPIPE_PASS_FWD && pass != UPIPE_PASS_BWD)) return UPIPE_EINVAL;
+  if (!bytes || pass < UPIPE_PASS_FWD || pass > UPIPE_PASS_BWD_RECOMPUTE) return UPIPE_EINVAL;
   Shape s;
   int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
   if (rc != UPIPE_OK) return rc;
+  if (pass == UPIPE_PASS_BWD_RECOMPUTE && !s.proj) return UPIPE_EINVAL;
   *bytes = make_plan(s, pass).total;
   return UPIPE_OK;
 }
@@ -361,6 +372,7 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
 
     // 2. causal attention of the chunk's heads; stores O and LSE
     FwdArgs fa;
+    memset(&fa, 0, sizeof(fa));
     fa.q = q_rm;
     fa.k = k_rm;
     fa.v = v_rm;
@@ -368,6 +380,7 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     fa.group = s.G;
     fa.q_head0 = ch.h0;
     fa.kv_head0 = ch.g0;
+    fa.o_head0 = 0;
     fa.o = o_saved;
     fa.o_ld = (int64_t)s.Hq * d;
     fa.lse = lse;
@@ -407,16 +420,20 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   Shape s;
   int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
   if (rc != UPIPE_OK) return rc;
-  rc = check_common(s, rope_theta, x, w_qkv, w_o, workspace, workspace_bytes, UPIPE_PASS_BWD);
+  // o_saved == NULL: recompute each chunk's attention output (projection mode)
+  const bool recompute = o_saved == nullptr;
+  if (recompute && !s.proj) return UPIPE_EINVAL;
+  const int pass = recompute ? UPIPE_PASS_BWD_RECOMPUTE : UPIPE_PASS_BWD;
+  rc = check_common(s, rope_theta, x, w_qkv, w_o, workspace, workspace_bytes, pass);
   if (rc != UPIPE_OK) return rc;
-  if (!o_saved || !lse || !dy || !dx) return UPIPE_EINVAL;
+  if (!lse || !dy || !dx) return UPIPE_EINVAL;
   if (s.proj != (dw_qkv != nullptr) || s.proj != (dw_o != nullptr)) return UPIPE_EINVAL;
-  if (!aligned16(o_saved) || !aligned16(lse) || !aligned16(dy) || !aligned16(dx) ||
+  if ((o_saved && !aligned16(o_saved)) || !aligned16(lse) || !aligned16(dy) || !aligned16(dx) ||
       (dw_qkv && !aligned16(dw_qkv)) || (dw_o && !aligned16(dw_o)))
     return UPIPE_EINVAL;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const Plan p = make_plan(s, UPIPE_PASS_BWD);
+  const Plan p = make_plan(s, pass);
   const RopeTable rope = make_rope(rope_theta, s.d);
   const int d = s.d;
   const int64_t qkv_ld = (int64_t)(s.Hq + 2 * s.Hkv) * d;
@@ -431,6 +448,8 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   float* dk_acc = at<float>(workspace, p.dk_acc);
   float* dv_acc = at<float>(workspace, p.dv_acc);
   float* dw_acc = at<float>(workspace, p.dw_acc);
+  uint16_t* o_c = at<uint16_t>(workspace, p.o_c);
+  uint16_t* v_t = at<uint16_t>(workspace, p.v_t);
 
   // the weight-gradient accumulator starts at zero; each conversion pass
   // clears what it consumed
@@ -466,10 +485,43 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pa.v_out_f16 = 0;
     UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_qkv(pa, rope, st));
 
+    // 1b. full recompute: the forward's attention of the chunk's heads again,
+    // from the same q, k and (fp16 tile) v, into o_c; it equals the
+    // forward's O bit for bit.  Its LSE output is scratch in lse2.
+    if (recompute) {
+      if (ch.kv_first) {
+        PrepArgs pv = pa;
+        pv.v_only = 1;
+        pv.v_rm = v_t;
+        pv.v_out_f16 = 1;
+        pv.v_tiles = 1;
+        UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_qkv(pv, rope, st));
+      }
+      FwdArgs fa;
+      memset(&fa, 0, sizeof(fa));
+      fa.q = q_rm;
+      fa.k = k_rm;
+      fa.v = v_t;
+      fa.nh = s.hc;
+      fa.group = s.G;
+      fa.q_head0 = ch.h0;
+      fa.kv_head0 = ch.g0;
+      fa.o_head0 = ch.h0;
+      fa.o = o_c;
+      fa.o_ld = (int64_t)s.hc * d;
+      fa.lse = lse2;
+      fa.L = s.L;
+      fa.Lp = s.Lp;
+      fa.scale_log2 = kLog2e / sqrtf((float)d);
+      UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_FWD, launch_flash_fwd(fa, st));
+    }
+    const uint16_t* o_chunk = recompute ? o_c : o_saved + (int64_t)ch.h0 * d;
+    const int64_t o_chunk_ld = recompute ? (int64_t)s.hc * d : (int64_t)s.Hq * d;
+
     // 2. dO of the chunk's heads (dy W_o[:, cols] or the given dO) and dW_o
     PrepDoutArgs pd;
-    pd.o = o_saved + (int64_t)ch.h0 * d;
-    pd.o_ld = (int64_t)s.Hq * d;
+    pd.o = o_chunk;
+    pd.o_ld = o_chunk_ld;
     pd.lse = lse + (int64_t)ch.h0 * s.L;
     pd.nh = s.hc;
     pd.do_rm = do_rm;
@@ -500,8 +552,8 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       memset(&w, 0, sizeof(w));
       w.A = dy;
       w.lda = s.D;
-      w.B = o_saved + (int64_t)ch.h0 * d;
-      w.ldb = (int64_t)s.Hq * d;
+      w.B = o_chunk;
+      w.ldb = o_chunk_ld;
       w.C = dw_acc;
       w.M = s.D;
       w.N = s.hc * d;

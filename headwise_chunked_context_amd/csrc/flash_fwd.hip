@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   const float l_tot = half_sum(l_run);
   if (my_q >= L) return;
   const float inv = 1.f / l_tot;
-  const int hg = a.q_head0 + head;
+  const int hg = a.q_head0 - a.o_head0 + head;
   uint16_t* orow = a.o + (int64_t)my_q * a.o_ld + (int64_t)hg * 128;
 #pragma unroll
   for (int db = 0; db < 4; ++db)

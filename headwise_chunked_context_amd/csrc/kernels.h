@@ -72,6 +72,7 @@ struct PrepArgs {
   int v_out_f16;           // write v as fp16 (else bf16)
   int v_tiles;             // write v (fp16) as the forward's transposed
                            // 64-key tiles instead of row-major (see prep.hip)
+  int v_only;              // only the v heads (the q and k heads are skipped)
 };
 hipError_t launch_prep_qkv(const PrepArgs& a, const RopeTable& t, hipStream_t s);
 
@@ -102,9 +103,10 @@ struct FwdArgs {
   int group;            // G = Hq / Hkv
   int q_head0;          // global index of the chunk's first q head
   int kv_head0;         // global index of kv buffer 0
-  uint16_t* o;          // o_saved [L][o_ld]; head h at column h*128
+  int o_head0;          // global q head stored at column 0 of o / row 0 of lse
+  uint16_t* o;          // [L][o_ld]; q head h at column (h - o_head0)*128
   int64_t o_ld;
-  float* lse;           // [Hq][L]
+  float* lse;           // [.][L]; q head h at row h - o_head0
   int64_t L, Lp;
   float scale_log2;     // log2(e) / sqrt(d)
 };

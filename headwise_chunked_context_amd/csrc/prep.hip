@@ -74,7 +74,7 @@ __device__ void write_v_tiles(const PrepArgs& a, const uint16_t* src, uint16_t* 
 
 // one workgroup per 64 rows of one head slot (q heads, then k, then v)
 __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a, RopeTable t) {
-  const int slot = blockIdx.y;
+  const int slot = blockIdx.y + (a.v_only ? a.nq + a.nkv : 0);
   const int64_t r0 = (int64_t)blockIdx.x * ROWS;
   const uint16_t* src;
   uint16_t* dst;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void zero_kernel(u32x4* p, int64_t n16) {
 }  // namespace
 
 hipError_t launch_prep_qkv(const PrepArgs& a, const RopeTable& t, hipStream_t s) {
-  dim3 grid((unsigned)(a.Lp / ROWS), a.nq + 2 * a.nkv);
+  dim3 grid((unsigned)(a.Lp / ROWS), a.v_only ? a.nkv : a.nq + 2 * a.nkv);
   hipLaunchKernelGGL(prep_qkv_kernel, grid, dim3(256), 0, s, a, t);
   return hipGetLastError();
 }

@@ -73,11 +73,13 @@ extern "C" {
 
 #define UPIPE_PASS_FWD 0
 #define UPIPE_PASS_BWD 1
+#define UPIPE_PASS_BWD_RECOMPUTE 2  /* upipe_attn_bwd with o_saved == NULL */
 
 /*
  * Workspace size query.  Writes to *bytes the workspace that upipe_attn_fwd
- * (pass = UPIPE_PASS_FWD) or upipe_attn_bwd (pass = UPIPE_PASS_BWD) needs for
- * these shapes.  The size is affine in head_chunk (per-chunk q-side buffers
+ * (pass = UPIPE_PASS_FWD), upipe_attn_bwd (pass = UPIPE_PASS_BWD) or
+ * upipe_attn_bwd in full-recompute mode (pass = UPIPE_PASS_BWD_RECOMPUTE,
+ * projection mode only) needs for these shapes.  The size is affine in head_chunk (per-chunk q-side buffers
  * plus the resident KV group): choosing head_chunk is how a caller fits the
  * layer into its memory budget (chunk-size ablation paragraph of the
  * talk write-up).  Returns UPIPE_OK or the error the entry point itself would
@@ -111,12 +113,22 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
  * Backward pass (chain rule of the forward; q/k/v are recomputed per chunk
  * from x, so only o_saved and lse are kept from the forward).
  *  x, w_qkv, w_o   as in upipe_attn_fwd
- *  o_saved, lse    the forward's outputs for the same inputs
+ *  o_saved, lse    the forward's outputs for the same inputs.  In projection
+ *           mode o_saved may be NULL ("full recompute"): each chunk's
+ *           attention output is then recomputed from the recomputed q/k/v
+ *           (4*head_dim FLOPs more per causal pair and q head) into
+ *           per-chunk workspace, so nothing of size L*Hq*head_dim has to
+ *           outlive the forward: activation checkpointing, one step of the
+ *           memory progression in "Untied Ulysses Pushes Llama-3-8B Training
+ *           to 5 Million Tokens", applied to this layer's own saved output.
+ *           Needs the UPIPE_PASS_BWD_RECOMPUTE workspace; the results equal
+ *           those of the o_saved call bit for bit.
  *  dy       [L, hidden] bf16 upstream gradient of y, or dO [L, Hq*head_dim]
  *  dx       [L, hidden] bf16 out, or dqkv [L, (Hq+2Hkv)*head_dim] (hidden == 0)
  *  dw_qkv   [(Hq+2Hkv)*head_dim, hidden] bf16 out, NULL iff hidden == 0
  *  dw_o     [hidden, Hq*head_dim] bf16 out, NULL iff hidden == 0
  *  workspace, workspace_bytes: at least the UPIPE_PASS_BWD query size
+ *           (UPIPE_PASS_BWD_RECOMPUTE when o_saved is NULL)
  */
 int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
                    int32_t head_dim, double rope_theta, int32_t head_chunk,

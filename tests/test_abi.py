@@ -63,6 +63,10 @@ def _ws(L, D, nq, nkv, d, hc, pss):
     ((1024, 1536, 12, 3, 128, 6, 1), B.UPIPE_ECHUNK),        # G = 4, chunk 6 straddles
     ((1024, 1024, 8, 2, 128, 0, 0), B.UPIPE_EINVAL),
     ((1024, 1024, 8, 2, 128, 2, 7), B.UPIPE_EINVAL),         # bad pass
+    ((1024, 1024, 8, 2, 128, 2, 3), B.UPIPE_EINVAL),
+    ((1024, 1024, 8, 2, 128, 2, -1), B.UPIPE_EINVAL),
+    ((1024, 1024, 8, 2, 128, 2, 2), B.UPIPE_OK),             # recompute backward
+    ((1024, 0, 8, 2, 128, 2, 2), B.UPIPE_EINVAL),            # ... needs projection mode
 ])
 def test_workspace_query_status(args, code):
     rc, _ = _ws(*args)
@@ -74,10 +78,12 @@ def test_workspace_query_null_output():
     assert rc == B.UPIPE_EINVAL
 
 
-@pytest.mark.parametrize("pss", [B.PASS_FWD, B.PASS_BWD])
+@pytest.mark.parametrize("pss", [B.PASS_FWD, B.PASS_BWD, B.PASS_BWD_RECOMPUTE])
 @pytest.mark.parametrize("shape", [(262144, 5120, 8, 1), (524288, 0, 4, 1), (32768, 4096, 32, 8)])
 def test_workspace_affine_and_shrinking_in_chunk(shape, pss):
     L, D, nq, nkv = shape
+    if pss == B.PASS_BWD_RECOMPUTE and D == 0:
+        pytest.skip("the recompute backward exists in projection mode only")
     G = nq // nkv
     chunks = [c for c in (1, 2, 4, 8, 16, 32) if nq % c == 0 and (c % G == 0 or G % c == 0)]
     sizes = {c: _ws(L, D, nq, nkv, 128, c, pss)[1] for c in chunks}
@@ -168,3 +174,31 @@ def test_exact_workspace_size_is_accepted_by_the_check():
     rc, need = _ws(1024, 1024, 8, 2, 128, 2, B.PASS_BWD)
     assert rc == 0 and need > 0
     assert _bwd(wsb=need - 1) == B.UPIPE_EWORKSPACE
+
+
+@pytest.mark.parametrize("L,hc", [(1000, 1), (1024, 2), (4097, 8)])
+def test_recompute_workspace_adds_chunk_output_and_v_tiles(L, hc):
+    """The recompute backward needs the chunk's attention output [L][hc*128]
+    bf16 and the V tiles of the KV heads it touches [kc][Lp][128] fp16 on top
+    of the ordinary backward's workspace (each buffer 256-byte aligned)."""
+    nq, nkv = 8, 2
+    G = nq // nkv
+    kc = hc // G if hc >= G else 1
+    Lp = (L + 255) // 256 * 256
+    up = lambda v: (v + 255) // 256 * 256
+    _, base = _ws(L, 1024, nq, nkv, 128, hc, B.PASS_BWD)
+    _, rec = _ws(L, 1024, nq, nkv, 128, hc, B.PASS_BWD_RECOMPUTE)
+    assert rec - base == up(L * hc * 128 * 2) + up(kc * Lp * 128 * 2)
+
+
+def test_bwd_recompute_argument_checks():
+    # o_saved = NULL selects the recompute backward: projection mode only
+    assert _bwd(o=None, D=0, wqkv=None, wo=None, dwqkv=None, dwo=None) == B.UPIPE_EINVAL
+    # ... and it needs the larger workspace
+    _, base = _ws(1024, 1024, 8, 2, 128, 2, B.PASS_BWD)
+    _, rec = _ws(1024, 1024, 8, 2, 128, 2, B.PASS_BWD_RECOMPUTE)
+    assert _bwd(o=None, wsb=base) == B.UPIPE_EWORKSPACE
+    assert _bwd(o=None, wsb=rec - 1) == B.UPIPE_EWORKSPACE
+    assert _bwd(o=None, lse=None, wsb=rec) == B.UPIPE_EINVAL   # the saved LSE is still needed
+    # with o_saved given, the ordinary workspace suffices
+    assert _bwd(wsb=base - 1) == B.UPIPE_EWORKSPACE
