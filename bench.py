@@ -140,6 +140,8 @@ def main() -> int:
     ap.add_argument("--seq-len", type=int, default=0, help="override L (not a metric run)")
     ap.add_argument("--recompute", action="store_true",
                     help="backward without the saved attention output (recomputed per chunk)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="overlap the forward's next-chunk projection on a second stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -158,6 +160,7 @@ def main() -> int:
     import headwise_chunked_context_amd as lib
     import synthetic
 
+    lib.pipeline_enable(args.pipeline)
     w = synthetic.WORKLOADS[args.workload]
     if args.chunk:
         w = w.with_(head_chunk=args.chunk)
@@ -177,7 +180,7 @@ def main() -> int:
     x, wq, wo, dy = (to_dev(inp[k]) for k in ("x", "w_qkv", "w_o", "dy"))
     del inp
     hidden = w.hidden
-    ws_f = lib.workspace_bytes(w.L, hidden, w.n_q, w.n_kv, w.head_dim, hc, lib.PASS_FWD)
+    ws_f = lib.workspace_bytes(w.L, hidden, w.n_q, w.n_kv, w.head_dim, hc, lib.fwd_pass())
     bwd_pass = lib.PASS_BWD_RECOMPUTE if args.recompute else lib.PASS_BWD
     ws_b = lib.workspace_bytes(w.L, hidden, w.n_q, w.n_kv, w.head_dim, hc, bwd_pass)
     # one workspace, sized for the larger pass, reused by every call
@@ -283,6 +286,7 @@ def main() -> int:
             "causal": True,
             "parallelism": "single GPU (one GPU's share; no collectives)",
             "backward": "recompute attention output" if args.recompute else "saved attention output",
+            "pipeline": args.pipeline,
         },
         "model_flops_per_step": flops,
         "roofline": roofline,

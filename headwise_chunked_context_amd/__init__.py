@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     PASS_BWD,
     PASS_BWD_RECOMPUTE,
     PASS_FWD,
+    PASS_FWD_PIPELINED,
     UPIPE_ECHUNK,
     UPIPE_EHIP,
     UPIPE_EINVAL,
@@ -18,7 +19,9 @@ from .binding import (  # noqa: F401
     UpipeError,
     attn_bwd,
     attn_fwd,
+    fwd_pass,
     lib,
+    pipeline_enable,
     profile_enable,
     profile_read,
     strerror,

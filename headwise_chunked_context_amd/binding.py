@@ -22,6 +22,8 @@ UPIPE_EHIP = -5
 PASS_FWD = 0
 PASS_BWD = 1
 PASS_BWD_RECOMPUTE = 2
+PASS_FWD_PIPELINED = 3
+_pipeline = False
 
 # names declared in include/upipe_attn.h
 EXPORTS = (
@@ -30,6 +32,7 @@ EXPORTS = (
     "upipe_attn_bwd",
     "upipe_profile_enable",
     "upipe_profile_read",
+    "upipe_pipeline_enable",
     "upipe_strerror",
     "upipe_version",
 )
@@ -76,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.upipe_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]
     L.upipe_profile_read.restype = ctypes.c_int
+    L.upipe_pipeline_enable.argtypes = [ctypes.c_int]
+    L.upipe_pipeline_enable.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -92,6 +97,21 @@ def workspace_bytes(L: int, hidden: int, n_q: int, n_kv: int, head_dim: int, hea
     if rc != UPIPE_OK:
         raise UpipeError(rc, "upipe_attn_workspace_bytes")
     return out.value
+
+
+def pipeline_enable(on: bool) -> None:
+    """Two-slot pipelining of the forward on a second stream (default off;
+    needs the PASS_FWD_PIPELINED workspace while on)."""
+    global _pipeline
+    rc = lib().upipe_pipeline_enable(1 if on else 0)
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_pipeline_enable")
+    _pipeline = bool(on)
+
+
+def fwd_pass() -> int:
+    """Workspace pass of upipe_attn_fwd under the current pipelining setting."""
+    return PASS_FWD_PIPELINED if _pipeline else PASS_FWD
 
 
 def profile_enable(on: bool) -> None:
@@ -147,7 +167,7 @@ def attn_fwd(x, w_qkv, w_o, n_q: int, n_kv: int, head_chunk: int, theta: float,
     y = torch.empty(L, hidden, dtype=torch.bfloat16, device=dev) if proj else None
     o_saved = torch.empty(L, n_q * head_dim, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(n_q, L, dtype=torch.float32, device=dev)
-    ws_n = workspace_bytes(L, hidden, n_q, n_kv, head_dim, head_chunk, PASS_FWD)
+    ws_n = workspace_bytes(L, hidden, n_q, n_kv, head_dim, head_chunk, fwd_pass())
     ws = _workspace(ws_n, dev, workspace)
     rc = lib().upipe_attn_fwd(L, hidden, n_q, n_kv, head_dim, float(theta), head_chunk,
                               _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(y), _ptr(o_saved), _ptr(lse),

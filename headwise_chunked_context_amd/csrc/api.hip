@@ -11,6 +11,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -91,6 +92,7 @@ struct Plan {
   size_t staging;              // [L][(hc+2kc)d] bf16 GEMM output / gradient staging
   size_t q_rm;                 // [hc][Lp][d] bf16, rotated
   size_t k_rm, v_rm;           // [kc][Lp][d] bf16 (k rotated; v fp16 in the forward)
+  size_t q_rm2, k_rm2, v_rm2;  // the same, second slot (forward pipeline)
   size_t do_rm;                // [hc][Lp][d] bf16 (bwd)
   size_t lse2, dvec;           // [hc][Lp] fp32 (bwd)
   size_t dk_acc, dv_acc;       // [kc][Lp][d] fp32 (bwd, only when a group spans chunks)
@@ -117,6 +119,14 @@ Plan make_plan(const Shape& s, int pass) {
   p.q_rm = take(hc * head_bf16);
   p.k_rm = take(kc * head_bf16);
   p.v_rm = take(kc * head_bf16);
+  if (pass == UPIPE_PASS_FWD_PIPELINED) {
+    // the next chunk's q/k/v are prepared while this chunk's attention runs
+    p.q_rm2 = take(hc * head_bf16);
+    p.k_rm2 = take(kc * head_bf16);
+    p.v_rm2 = take(kc * head_bf16);
+  } else {
+    p.q_rm2 = p.k_rm2 = p.v_rm2 = no;
+  }
   p.o_c = p.v_t = no;
   if (pass == UPIPE_PASS_BWD || pass == UPIPE_PASS_BWD_RECOMPUTE) {
     p.do_rm = take(hc * head_bf16);
@@ -208,6 +218,40 @@ hipError_t timed(int kind, hipStream_t st, F&& launch) {
 
 #define UPIPE_LAUNCH(kind, expr) UPIPE_TRY(timed((kind), st, [&]() { return (expr); }))
 
+// ---- two-slot pipeline: a second stream per device.  While chunk c's
+// attention runs on the caller's stream, chunk c+1's projection and layout
+// pass run on this one into the other slot of q/k/v buffers; events order
+// the slot hand-over in both directions.  The stream and its events are
+// created on a device's first pipelined call and kept for the process.
+constexpr int kMaxDevices = 64;
+struct Side {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t ready[2] = {nullptr, nullptr};  // slot's q/k/v prepared
+  hipEvent_t done[2] = {nullptr, nullptr};   // slot's attention finished
+};
+Side g_side[kMaxDevices];
+std::mutex g_side_mu;
+bool g_pipeline = false;
+
+int side_stream(Side** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return UPIPE_EHIP;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  Side& sd = g_side[dev];
+  if (!sd.stream) {
+    hipEvent_t* evs[5] = {&sd.fork, &sd.ready[0], &sd.ready[1], &sd.done[0], &sd.done[1]};
+    for (hipEvent_t* e : evs)
+      if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) return UPIPE_EHIP;
+    if (hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking) != hipSuccess) {
+      sd.stream = nullptr;
+      return UPIPE_EHIP;
+    }
+  }
+  *out = &sd;
+  return UPIPE_OK;
+}
+
 struct Chunk {
   int h0;        // first q head
   int g0;        // first KV group touched
@@ -266,6 +310,11 @@ extern "C" {
 
 int upipe_version(void) { return 100; }
 
+int upipe_pipeline_enable(int on) {
+  g_pipeline = on != 0;
+  return UPIPE_OK;
+}
+
 int upipe_profile_enable(int on) {
   for (int k = 0; k < kKinds; ++k) {
     for (auto& pr : g_prof.rec[k]) {
@@ -307,7 +356,7 @@ const char* upipe_strerror(int status) {
 int upipe_attn_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t n_q_heads,
                                int32_t n_kv_heads, int32_t head_dim, int32_t head_chunk,
                                int32_t pass, size_t* bytes) {
-  if (!bytes || pass < UPIPE_PASS_FWD || pass > UPIPE_PASS_BWD_RECOMPUTE) return UPIPE_EINVAL;
+  if (!bytes || pass < UPIPE_PASS_FWD || pass > UPIPE_PASS_FWD_PIPELINED) return UPIPE_EINVAL;
   Shape s;
   int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
   if (rc != UPIPE_OK) return rc;
@@ -323,29 +372,52 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   Shape s;
   int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
   if (rc != UPIPE_OK) return rc;
-  rc = check_common(s, rope_theta, x, w_qkv, w_o, workspace, workspace_bytes, UPIPE_PASS_FWD);
+  const int pass = g_pipeline ? UPIPE_PASS_FWD_PIPELINED : UPIPE_PASS_FWD;
+  rc = check_common(s, rope_theta, x, w_qkv, w_o, workspace, workspace_bytes, pass);
   if (rc != UPIPE_OK) return rc;
   if (!o_saved || !lse || s.proj != (y != nullptr)) return UPIPE_EINVAL;
   if (!aligned16(o_saved) || !aligned16(lse) || (y && !aligned16(y))) return UPIPE_EINVAL;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const Plan p = make_plan(s, UPIPE_PASS_FWD);
+  const Plan p = make_plan(s, pass);
   const RopeTable rope = make_rope(rope_theta, s.d);
   const int d = s.d;
   uint16_t* staging = at<uint16_t>(workspace, p.staging);
-  uint16_t* q_rm = at<uint16_t>(workspace, p.q_rm);
-  uint16_t* k_rm = at<uint16_t>(workspace, p.k_rm);
-  uint16_t* v_rm = at<uint16_t>(workspace, p.v_rm);
+  uint16_t* q_slot[2] = {at<uint16_t>(workspace, p.q_rm), at<uint16_t>(workspace, p.q_rm2)};
+  uint16_t* k_slot[2] = {at<uint16_t>(workspace, p.k_rm), at<uint16_t>(workspace, p.k_rm2)};
+  uint16_t* v_slot[2] = {at<uint16_t>(workspace, p.v_rm), at<uint16_t>(workspace, p.v_rm2)};
   const int64_t qkv_ld = (int64_t)(s.Hq + 2 * s.Hkv) * d;
   const int width = (s.hc + 2 * s.kc) * d;
+  const int nchunks = s.Hq / s.hc;
 
-  for (int c = 0; c < s.Hq / s.hc; ++c) {
+  // Chunk c's q uses slot c % 2; a KV group's k/v use the slot after the
+  // previous group's.  The projection half of chunk c waits for chunk
+  // c - 2's attention (the last reader of its q slot; a KV slot's last
+  // reader is at least as early), the attention of chunk c for its
+  // projection half.
+  Side* side = nullptr;
+  hipStream_t sb = st;
+  if (g_pipeline && nchunks > 1) {
+    rc = side_stream(&side);
+    if (rc != UPIPE_OK) return rc;
+    sb = side->stream;
+    UPIPE_TRY(hipEventRecord(side->fork, st));
+    UPIPE_TRY(hipStreamWaitEvent(sb, side->fork, 0));
+  }
+  int kslot = 1;
+  for (int c = 0; c < nchunks; ++c) {
     const Chunk ch = chunk_info(s, c);
+    const int qslot = side ? c & 1 : 0;
+    if (ch.kv_first) kslot = side ? kslot ^ 1 : 0;
+    uint16_t* q_rm = q_slot[qslot];
+    uint16_t* k_rm = k_slot[kslot];
+    uint16_t* v_rm = v_slot[kslot];
+    if (side && c >= 2) UPIPE_TRY(hipStreamWaitEvent(sb, side->done[qslot], 0));
     // 1. chunked QKV projection (or pick the given q/k/v columns) + RoPE
     PrepArgs pa;
     memset(&pa, 0, sizeof(pa));
     if (s.proj) {
-      rc = project_chunk(s, ch, x, w_qkv, staging, rope, st);
+      rc = project_chunk(s, ch, x, w_qkv, staging, rope, sb);
       if (rc != UPIPE_OK) return rc;
       pa.src_q = staging;
       pa.src_k = staging + s.hc * d;
@@ -368,7 +440,11 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pa.v_src_f16 = s.proj ? 1 : 0;
     pa.v_out_f16 = 1;
     pa.v_tiles = 1;
-    UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_qkv(pa, rope, st));
+    UPIPE_TRY(timed(UPIPE_KERNEL_PREP, sb, [&]() { return launch_prep_qkv(pa, rope, sb); }));
+    if (side) {
+      UPIPE_TRY(hipEventRecord(side->ready[qslot], sb));
+      UPIPE_TRY(hipStreamWaitEvent(st, side->ready[qslot], 0));
+    }
 
     // 2. causal attention of the chunk's heads; stores O and LSE
     FwdArgs fa;
@@ -388,6 +464,7 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     fa.Lp = s.Lp;
     fa.scale_log2 = kLog2e / sqrtf((float)d);
     UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_FWD, launch_flash_fwd(fa, st));
+    if (side) UPIPE_TRY(hipEventRecord(side->done[qslot], st));
   }
 
   // 3. output projection: y = sum over chunks of O_c W_o[:, cols(c)]^T.  The

@@ -51,6 +51,12 @@
  *    null stream) and is asynchronous: the call returns before the GPU is
  *    done.  The library never synchronizes.  Calls that share a workspace
  *    must be ordered on one stream.
+ *  - Calls run on the current HIP device.  With pipelining enabled (off by
+ *    default, see upipe_pipeline_enable) the forward also uses a second
+ *    stream of the library's own, forked from and joined back into `stream`
+ *    with events, so work after the call on `stream` sees every result.
+ *    Calls on one device must not run concurrently from several host
+ *    threads.
  *  - Outputs are fully overwritten (never accumulated into).
  */
 #ifndef UPIPE_ATTN_H
@@ -74,12 +80,14 @@ extern "C" {
 #define UPIPE_PASS_FWD 0
 #define UPIPE_PASS_BWD 1
 #define UPIPE_PASS_BWD_RECOMPUTE 2  /* upipe_attn_bwd with o_saved == NULL */
+#define UPIPE_PASS_FWD_PIPELINED 3  /* upipe_attn_fwd with pipelining enabled */
 
 /*
  * Workspace size query.  Writes to *bytes the workspace that upipe_attn_fwd
- * (pass = UPIPE_PASS_FWD), upipe_attn_bwd (pass = UPIPE_PASS_BWD) or
- * upipe_attn_bwd in full-recompute mode (pass = UPIPE_PASS_BWD_RECOMPUTE,
- * projection mode only) needs for these shapes.  The size is affine in head_chunk (per-chunk q-side buffers
+ * (pass = UPIPE_PASS_FWD; UPIPE_PASS_FWD_PIPELINED while pipelining is
+ * enabled), upipe_attn_bwd (pass = UPIPE_PASS_BWD) or upipe_attn_bwd in
+ * full-recompute mode (pass = UPIPE_PASS_BWD_RECOMPUTE, projection mode only)
+ * needs for these shapes.  The size is affine in head_chunk (per-chunk q-side buffers
  * plus the resident KV group): choosing head_chunk is how a caller fits the
  * layer into its memory budget (chunk-size ablation paragraph of the
  * talk write-up).  Returns UPIPE_OK or the error the entry point itself would
@@ -100,7 +108,8 @@ int upipe_attn_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t n_q_head
  *  lse      [Hq, L] fp32 out: natural-log sum of exp of the scaled scores of
  *           each query row; upipe_attn_bwd reads it back
  *  workspace, workspace_bytes: caller-owned scratch of at least the size the
- *           query returns for UPIPE_PASS_FWD; contents on entry are ignored
+ *           query returns for UPIPE_PASS_FWD (UPIPE_PASS_FWD_PIPELINED while
+ *           pipelining is enabled); contents on entry are ignored
  *  stream   hipStream_t or NULL
  */
 int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
@@ -162,6 +171,23 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
 #define UPIPE_KERNEL_FINALIZE 5
 int upipe_profile_enable(int on);
 int upipe_profile_read(int kind, double* total_ms, int64_t* launches);
+
+/*
+ * Two-slot pipelining of the forward (off by default): chunk c+1's QKV
+ * projection and RoPE/layout pass run on a second stream, into a second set
+ * of q/k/v workspace buffers, while chunk c's attention runs on the caller's
+ * stream (the overlap of the next group's projection with the current
+ * group's attention, "Untied Ulysses Pushes Llama-3-8B Training to 5 Million
+ * Tokens", Untied Ulysses section).  While enabled, upipe_attn_fwd needs the
+ * UPIPE_PASS_FWD_PIPELINED workspace (else UPIPE_EWORKSPACE).  The stream
+ * (default priority) and five events are created on a device's first
+ * pipelined call and kept until the process ends; no device memory is
+ * allocated.  Results are identical either way.  On one GPU the overlap
+ * gains nothing measurable (the attention kernels keep every CU busy, so the
+ * projection only takes CUs from them), hence off by default.  Process-wide
+ * setting; returns UPIPE_OK.
+ */
+int upipe_pipeline_enable(int on);
 
 /* Static, human-readable text for a status code.  Never NULL. */
 const char* upipe_strerror(int status);

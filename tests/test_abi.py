@@ -63,8 +63,9 @@ def _ws(L, D, nq, nkv, d, hc, pss):
     ((1024, 1536, 12, 3, 128, 6, 1), B.UPIPE_ECHUNK),        # G = 4, chunk 6 straddles
     ((1024, 1024, 8, 2, 128, 0, 0), B.UPIPE_EINVAL),
     ((1024, 1024, 8, 2, 128, 2, 7), B.UPIPE_EINVAL),         # bad pass
-    ((1024, 1024, 8, 2, 128, 2, 3), B.UPIPE_EINVAL),
+    ((1024, 1024, 8, 2, 128, 2, 4), B.UPIPE_EINVAL),
     ((1024, 1024, 8, 2, 128, 2, -1), B.UPIPE_EINVAL),
+    ((1024, 0, 8, 2, 128, 2, 3), B.UPIPE_OK),                # pipelined forward
     ((1024, 1024, 8, 2, 128, 2, 2), B.UPIPE_OK),             # recompute backward
     ((1024, 0, 8, 2, 128, 2, 2), B.UPIPE_EINVAL),            # ... needs projection mode
 ])
@@ -78,7 +79,7 @@ def test_workspace_query_null_output():
     assert rc == B.UPIPE_EINVAL
 
 
-@pytest.mark.parametrize("pss", [B.PASS_FWD, B.PASS_BWD, B.PASS_BWD_RECOMPUTE])
+@pytest.mark.parametrize("pss", [B.PASS_FWD, B.PASS_BWD, B.PASS_BWD_RECOMPUTE, B.PASS_FWD_PIPELINED])
 @pytest.mark.parametrize("shape", [(262144, 5120, 8, 1), (524288, 0, 4, 1), (32768, 4096, 32, 8)])
 def test_workspace_affine_and_shrinking_in_chunk(shape, pss):
     L, D, nq, nkv = shape
@@ -202,3 +203,24 @@ def test_bwd_recompute_argument_checks():
     assert _bwd(o=None, lse=None, wsb=rec) == B.UPIPE_EINVAL   # the saved LSE is still needed
     # with o_saved given, the ordinary workspace suffices
     assert _bwd(wsb=base - 1) == B.UPIPE_EWORKSPACE
+
+
+def test_pipelined_forward_workspace_and_check():
+    """Pipelining adds a second slot of q [hc][Lp][128] and k, v [kc][Lp][128]
+    (bf16/fp16) to the forward workspace, and while it is enabled the forward
+    rejects a workspace of the one-slot size before any launch."""
+    L, hc, nq, nkv = 1000, 2, 8, 2
+    Lp = 1024
+    up = lambda v: (v + 255) // 256 * 256
+    _, one = _ws(L, 1024, nq, nkv, 128, hc, B.PASS_FWD)
+    _, two = _ws(L, 1024, nq, nkv, 128, hc, B.PASS_FWD_PIPELINED)
+    assert two - one == up(hc * Lp * 256) + 2 * up(1 * Lp * 256)
+    try:
+        hc_amd.pipeline_enable(True)
+        assert hc_amd.fwd_pass() == B.PASS_FWD_PIPELINED
+        assert _fwd(L=L, wsb=one) == B.UPIPE_EWORKSPACE
+        assert _fwd(L=L, wsb=two, o=None) == B.UPIPE_EINVAL
+    finally:
+        hc_amd.pipeline_enable(False)
+    assert hc_amd.fwd_pass() == B.PASS_FWD
+    assert _fwd(L=L, wsb=one - 1) == B.UPIPE_EWORKSPACE
