@@ -54,6 +54,19 @@ int check_shape(int64_t L, int32_t hidden, int32_t n_q, int32_t n_kv, int32_t he
   s->G = G;
   s->kc = hc >= G ? hc / G : 1;
   s->proj = hidden > 0;
+  // every launch must stay below 2^32 work-items (the dispatch packet's
+  // grid size is 32-bit): attention grids are Lp/128 workgroups per head
+  // (256 threads, 512 for dK/dV per KV head); the sequence-long GEMMs are
+  // 256 x 256 tiles of 512 threads, the weight-gradient GEMMs at most 32
+  // splits of them
+  const int64_t lim = (int64_t)UINT32_MAX;
+  const int64_t width = (int64_t)(hc + 2 * s->kc) * head_dim;
+  const int64_t wide = width > hidden ? width : hidden;
+  const int64_t mt = (s->Lp + 255) / 256;
+  if ((s->Lp / 128) * hc * 256 > lim || (s->Lp / 128) * s->kc * 512 > lim ||
+      mt * ((wide + 255) / 256) * 512 > lim ||
+      ((int64_t)(hidden + 255) / 256) * ((width + 255) / 256) * 32 * 512 > lim)
+    return UPIPE_EUNSUPPORTED;
   return UPIPE_OK;
 }
 
@@ -345,7 +358,7 @@ const char* upipe_strerror(int status) {
   switch (status) {
     case UPIPE_OK: return "ok";
     case UPIPE_EINVAL: return "invalid argument (sizes, head counts, pointers or theta)";
-    case UPIPE_EUNSUPPORTED: return "unsupported shape (head_dim must be 128, hidden a multiple of 128, L <= 2^24)";
+    case UPIPE_EUNSUPPORTED: return "unsupported shape (head_dim must be 128, hidden a multiple of 128, L <= 2^24, launch grids below 2^32 threads)";
     case UPIPE_ECHUNK: return "head_chunk must divide n_q_heads and not split a KV group's query heads";
     case UPIPE_EWORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than upipe_attn_workspace_bytes";
     case UPIPE_EHIP: return "HIP runtime error while launching a kernel";

@@ -75,10 +75,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   // round-robin, so workgroup i runs on XCD i % 8.  Renumber so that each
   // XCD receives one contiguous range of tiles (n fastest): the workgroups
   // an XCD runs together then share A row panels and B k-slices in its L2
-  // instead of every XCD fetching every panel.
-  const int gx = gridDim.x, gy = gridDim.y;
-  const int total = gx * gy * gridDim.z;
-  const int id = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  // instead of every XCD fetching every panel.  The grid is one-dimensional
+  // (gx * gy * splits workgroups), so no per-dimension grid limit applies.
+  const int gx = (p.N + BN - 1) / BN, gy = (p.M + BM - 1) / BM;
+  const int total = gridDim.x;
+  const int id = blockIdx.x;
   const int q8 = total >> 3, r8 = total & 7, xcd = id & 7, local = id >> 3;
   const int tile = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + local;
   const int n0 = (tile % gx) * BN;
@@ -347,7 +348,8 @@ __global__ __launch_bounds__(256) void acc_to_bf16_kernel(float* acc, int M, int
 }  // namespace
 
 hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, hipStream_t s) {
-  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, (a.K + a.k_per_split - 1) / a.k_per_split);
+  dim3 grid((unsigned)(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM) *
+                       ((a.K + a.k_per_split - 1) / a.k_per_split)));
   dim3 block(NT);
 #define UPIPE_GEMM_CASE(AK, BK_, E) hipLaunchKernelGGL((gemm_kernel<AK, BK_, E>), grid, block, 0, s, a)
   switch (layout) {

@@ -44,7 +44,13 @@
  *  - Supported: head_dim == 128, hidden a multiple of 128 (or 0),
  *    1 <= L <= 2^24, Hq % Hkv == 0, Hq % head_chunk == 0 and either
  *    head_chunk % G == 0 or G % head_chunk == 0 (G = Hq/Hkv), so that no chunk
- *    holds part of two KV groups' query heads.
+ *    holds part of two KV groups' query heads; and no kernel grid reaches
+ *    2^32 threads: with L_256 = L rounded up to 256, kc = the KV heads one
+ *    chunk touches and w = (head_chunk + 2 kc) * 128,
+ *    L_256 * head_chunk < 2^31, L_256 * kc < 2^30,
+ *    L_256 * max(hidden, w) < 2^39 and hidden * w < 2^34
+ *    (UPIPE_EUNSUPPORTED otherwise; all hold for L <= 2^24 with
+ *    head_chunk <= 32 and hidden <= 16384).
  *  - All checks run on the host before the first launch; on any error nothing
  *    is launched and outputs are untouched.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
@@ -72,7 +78,8 @@ extern "C" {
 /* Status codes. */
 #define UPIPE_OK 0
 #define UPIPE_EINVAL (-1)       /* bad size, count, or pointer combination        */
-#define UPIPE_EUNSUPPORTED (-2) /* head_dim != 128, hidden % 128 != 0, L > 2^24   */
+#define UPIPE_EUNSUPPORTED (-2) /* head_dim != 128, hidden % 128 != 0, L > 2^24,
+                                   or a kernel grid of 2^32 threads or more       */
 #define UPIPE_ECHUNK (-3)       /* head_chunk does not divide Hq or straddles a KV group */
 #define UPIPE_EWORKSPACE (-4)   /* workspace NULL, misaligned or smaller than required */
 #define UPIPE_EHIP (-5)         /* the HIP runtime reported an error at launch    */

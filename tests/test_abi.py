@@ -63,6 +63,13 @@ def _ws(L, D, nq, nkv, d, hc, pss):
     ((1024, 1536, 12, 3, 128, 6, 1), B.UPIPE_ECHUNK),        # G = 4, chunk 6 straddles
     ((1024, 1024, 8, 2, 128, 0, 0), B.UPIPE_EINVAL),
     ((1024, 1024, 8, 2, 128, 2, 7), B.UPIPE_EINVAL),         # bad pass
+    # launch grids of 2^32 threads or more are refused on the host
+    ((1 << 24, 16384, 32, 32, 128, 32, 1), B.UPIPE_OK),      # the documented sufficient bound
+    ((1 << 24, 0, 32, 32, 128, 32, 0), B.UPIPE_OK),
+    ((1 << 24, 0, 128, 128, 128, 128, 0), B.UPIPE_EUNSUPPORTED),  # L_256 * chunk = 2^31
+    ((1 << 24, 0, 64, 64, 128, 64, 0), B.UPIPE_EUNSUPPORTED),     # L_256 * kc = 2^30
+    ((1 << 24, 32768, 8, 8, 128, 1, 0), B.UPIPE_EUNSUPPORTED),    # L_256 * hidden = 2^39
+    ((4096, 1 << 22, 64, 64, 128, 64, 1), B.UPIPE_EUNSUPPORTED),  # hidden * w > 2^34
     ((1024, 1024, 8, 2, 128, 2, 4), B.UPIPE_EINVAL),
     ((1024, 1024, 8, 2, 128, 2, -1), B.UPIPE_EINVAL),
     ((1024, 0, 8, 2, 128, 2, 3), B.UPIPE_OK),                # pipelined forward
