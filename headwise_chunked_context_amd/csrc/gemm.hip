@@ -4,19 +4,22 @@
 //   NT  x . W_rows^T, O . W_o^T       (both operands k-contiguous)
 //   NN  dy . W_o[:, cols], dqkv . W   (B n-contiguous)
 //   TN  dy^T . O, dqkv^T . x          (both m/n-contiguous; K = L, split-K)
-// Workgroup tile 256 x 256, k step 32, on 512 threads: 8 waves, two per
+// Workgroup tile 256 x 256, k step 64, on 512 threads: 8 waves, two per
 // SIMD, each owning 128 x 64 of C as 4 x 2 blocks of
 // v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 128 registers).  (One wave
 // per SIMD with 128 x 128 each halves the LDS reads per MFMA but measured
-// 10-15% slower: a single wave cannot hide the LDS and copy latencies.)
+// slower, with and without software-pipelined operand reads.)
 // Operand tiles go straight from global memory to LDS by asynchronous
-// global->LDS copies, four k steps in flight (four LDS stages, 128 KB), so a
-// tile is requested three k steps before its MFMAs need it; the copies stage
-// the tiles as they lie in memory, no transposing stores:
-//  * a k-contiguous operand is [256 rows][32 k] with 64-byte rows and the
-//    16-byte chunk index XORed with (row / 4) % 4, so 16 lanes reading 16
+// global->LDS copies into two LDS stages of 64 KB: the copy of k step t+1
+// is issued right after the barrier that opens step t, so it lands during
+// step t's 32 MFMAs per wave.  (A k step of 32 with four stages, three
+// steps in flight, measured 4% slower: twice the barriers and operand-read
+// latency bubbles per MFMA.)  The copies stage the tiles as they lie in
+// memory, no transposing stores:
+//  * a k-contiguous operand is [256 rows][64 k] with 128-byte rows and the
+//    16-byte chunk index XORed with (row / 2) % 8, so 16 lanes reading 16
 //    rows at one k offset hit 16 different bank groups;
-//  * an m/n-contiguous operand is [32 k][256] kept as two [32][128] halves in
+//  * an m/n-contiguous operand is [64 k][256] kept as two [64][128] halves in
 //    the swizzled 256-byte-row layout of common.h and read with the LDS
 //    transpose read (ds_read_b64_tr_b16), which hands each lane eight
 //    consecutive k of one column.
@@ -28,19 +31,27 @@
 namespace upipe {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int WM = 2, WN = 4;               // waves along M and N
 constexpr int NT = 64 * WM * WN;            // threads
 constexpr int MB = BM / WM / 32;            // 32x32 blocks per wave along M
 constexpr int NB = BN / WN / 32;            // ... along N
-constexpr int STAGES = 4;
+constexpr int STAGES = BK == 32 ? 4 : 2;   // 128 KB of LDS either way
 static_assert(WM == 2, "the bf16 epilogue stages one 128-row half of C per wave row");
 constexpr int TILE = 256 * BK;              // elements of one operand tile
-constexpr int HALF = 128 * BK;              // one [32][128] half of an m/n-major tile
+constexpr int HALF = 128 * BK;              // one [BK][128] half of an m/n-major tile
+constexpr int CHUNKS = BK / 8;              // 16-byte chunks per k-major row
+constexpr int ROWS_PER_KB = 512 / BK;       // k-major rows per 1 KB copy block
 constexpr int STAGE = 2 * TILE;             // A and B tiles of one k step
 
+// k-major tile: rows of BK elements, the 16-byte chunk index XORed so that
+// 16 lanes reading 16 consecutive rows at one chunk hit distinct banks
+// (64-byte rows: by (row / 4) % 4; 128-byte rows: by (row / 2) % 8)
+__device__ __forceinline__ int kmaj_swz(int row) {
+  return BK == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
 __device__ __forceinline__ int kmaj_off(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 2) & 3)) << 3);
+  return row * BK + ((chunk ^ kmaj_swz(row)) << 3);
 }
 
 __device__ __forceinline__ int64_t seg_map(const RowSegments& s, int idx) {
@@ -91,34 +102,34 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   // ---- copy plan: each wave moves CPW consecutive 1 KB blocks of
   // the A tile and of the B tile; per lane a source pointer (k = 0 of the
   // split) and, for m/n-major operands, its k row within the tile
-  constexpr int CPW = 16 / (WM * WN);  // 16 blocks of 1 KB per operand tile
+  constexpr int CPW = (TILE / 512) / (WM * WN);  // 1 KB blocks per operand tile, per wave
   const uint16_t* asrc[CPW];
   const uint16_t* bsrc[CPW];
   int arow[CPW], brow[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int n = CPW * wave + i;
-    if (A_K) {  // 16 rows x 64 bytes per block
-      const int row = 16 * n + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+    if (A_K) {  // ROWS_PER_KB rows of 2 BK bytes per block
+      const int row = ROWS_PER_KB * n + lane / CHUNKS;
+      const int c = (lane % CHUNKS) ^ kmaj_swz(row);
       const int m = min(m0 + row, p.M - 1);
       asrc[i] = p.A + (int64_t)m * p.lda + kbeg + c * 8;
       arow[i] = 0;
     } else {    // 4 k rows x 256 bytes of one 128-column half per block
-      const int half = n >> 3, row = 4 * (n & 7) + (lane >> 4);
+      const int half = n / (BK / 4), row = 4 * (n % (BK / 4)) + (lane >> 4);
       const int c = (lane & 15) ^ swz(row);
       const int col = min(m0 + half * 128 + c * 8, p.M - 8);
       asrc[i] = p.A + (int64_t)kbeg * p.lda + col;
       arow[i] = row;
     }
     if (B_K) {
-      const int row = 16 * n + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int row = ROWS_PER_KB * n + lane / CHUNKS;
+      const int c = (lane % CHUNKS) ^ kmaj_swz(row);
       const int nn = min(n0 + row, p.N - 1);
       bsrc[i] = p.B + seg_map(p.bseg, nn) * p.ldb + kbeg + c * 8;
       brow[i] = 0;
     } else {
-      const int half = n >> 3, row = 4 * (n & 7) + (lane >> 4);
+      const int half = n / (BK / 4), row = 4 * (n % (BK / 4)) + (lane >> 4);
       const int c = (lane & 15) ^ swz(row);
       const int col = min(n0 + half * 128 + c * 8, p.N - 8);
       bsrc[i] = p.B + col;  // rows come from the segment map per k step
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
       if (B_K) {
         b = bsrc[i] + k0;
       } else {
-        // a 32-row k step never crosses a segment (segments are multiples of
+        // a BK-row k step never crosses a segment (segments are multiples of
         // 128): one uniform segment lookup per step, rows clamped only in a
         // split's last, partial step
         const int kb0 = kbeg + k0;
@@ -157,9 +168,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   };
 
   // per-lane LDS element offsets of the MFMA operands within a stage
-  int aoff[2], boff[2];
+  int aoff[BK / 16], boff[BK / 16];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < BK / 16; ++ks) {
     aoff[ks] = A_K ? kmaj_off(wm * (BM / WM) + l32, 2 * ks + g) : 0;
     boff[ks] = B_K ? kmaj_off(wn * (BN / WN) + l32, 2 * ks + g) : 0;
   }
@@ -178,9 +189,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's copies of step kt are done once at most the copies of the
     // (up to two) later steps already issued are outstanding
+    constexpr int PER = 2 * CPW;  // copies per wave per k step
     const int later = min(nk - 1 - kt, STAGES - 2);
-    if (later >= 2) wait_vmcnt<8>();
-    else if (later == 1) wait_vmcnt<4>();
+    if (later >= 2) wait_vmcnt<2 * PER>();
+    else if (later == 1) wait_vmcnt<PER>();
     else wait_vmcnt<0>();
     __syncthreads();  // every wave's copies of step kt landed; step kt-1 fully read
     const int k0 = kbeg + kt * BK;
@@ -348,6 +360,8 @@ __global__ __launch_bounds__(256) void acc_to_bf16_kernel(float* acc, int M, int
 }  // namespace
 
 hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, hipStream_t s) {
+  // k steps of BK must not read past a k-contiguous row, nor splits overlap
+  if (a.k_per_split % BK != 0 || (layout != GEMM_TN && a.K % BK != 0)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM) *
                        ((a.K + a.k_per_split - 1) / a.k_per_split)));
   dim3 block(NT);

@@ -33,9 +33,9 @@ struct GemmArgs {
   RowSegments bseg;
   void* C;            // bf16 [M][ldc], or an fp32 [M][N] accumulator (split-K atomics)
   int64_t ldc;
-  int M, N, K;        // M, N multiples of 8; K a multiple of 32 when an operand is
+  int M, N, K;        // M, N multiples of 8; K a multiple of 64 when an operand is
                       // k-contiguous (NT, NN); any K for TN (the tail is zeroed)
-  int k_per_split;    // multiple of 32; gridDim.z = ceil(K / k_per_split)
+  int k_per_split;    // multiple of 64; ceil(K / k_per_split) splits
   // bf16 store epilogue only: output columns n < rope_cols are rotated (RoPE,
   // position = row m, pair = (n % 128) / 2) in fp32 before the one rounding
   int rope_cols;
