@@ -19,8 +19,8 @@ What is computed, and where it comes from
   is run, the partial result is stored and the output projection of that chunk
   is accumulated into y (same section: compute one group of heads, store a
   partial result, move to the next group reusing the buffers).
-* Grouped-query attention (same page, same section: the method is tailored to
-  multi-query and grouped-query attention): q head h reads KV head h // G,
+* Grouped-query attention (same page, same section: the method is built for
+  layers where several query heads share one key/value head): q head h reads KV head h // G,
   G = Hq / Hkv.
 * Rotary position embedding (Builds-on list: RoFormer): consecutive pairs
   (2i, 2i+1) are rotated by angle p * theta^(-2i/d) at position p.
