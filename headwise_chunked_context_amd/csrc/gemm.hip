@@ -84,7 +84,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
 
   // XCD-aware tile order: the dispatcher deals workgroups to the 8 XCDs
   // round-robin, so workgroup i runs on XCD i % 8.  Renumber so that each
-  // XCD receives one contiguous range of tiles (n fastest): the workgroups
+  // XCD receives one contiguous range of tiles: the workgroups
   // an XCD runs together then share A row panels and B k-slices in its L2
   // instead of every XCD fetching every panel.  The grid is one-dimensional
   // (gx * gy * splits workgroups), so no per-dimension grid limit applies.
@@ -93,8 +93,17 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   const int id = blockIdx.x;
   const int q8 = total >> 3, r8 = total & 7, xcd = id & 7, local = id >> 3;
   const int tile = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + local;
-  const int n0 = (tile % gx) * BN;
-  const int m0 = ((tile / gx) % gy) * BM;
+  // Within a split, tiles go in bands of GM rows, down the band's rows
+  // first: the ~32 tiles one XCD runs at a time then span 8 row panels of A
+  // and 4 column panels of B instead of 2 and 16, so each panel fetched into
+  // the XCD's L2 serves more tiles.
+  constexpr int GM = 8;
+  const int t = tile % (gx * gy);
+  const int m_first = (t / (GM * gx)) * GM;
+  const int gm = min(gy - m_first, GM);
+  const int u = t % (GM * gx);
+  const int n0 = (u / gm) * BN;
+  const int m0 = (m_first + u % gm) * BM;
   const int kbeg = (tile / (gx * gy)) * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int nk = (kend - kbeg + BK - 1) / BK;
