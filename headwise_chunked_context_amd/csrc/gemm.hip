@@ -79,7 +79,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
+  // wave -> (wm, wn): the waves of a workgroup are dealt to the CU's four
+  // SIMDs round-robin (wave w on SIMD w % 4), so the two waves of a SIMD take
+  // columns from different halves of the tile (wn < 2 and wn >= 2): when a
+  // tile is only partly inside N (N % 256 == 128) every SIMD keeps one busy
+  // wave instead of two SIMDs keeping two
+  static_assert(WM == 2 && WN == 4, "wave mapping below");
+  const int wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * (wave >> 2);
   const int g = lane >> 5, l32 = lane & 31;
 
   // XCD-aware tile order: the dispatcher deals workgroups to the 8 XCDs
@@ -184,6 +190,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     boff[ks] = B_K ? kmaj_off(wn * (BN / WN) + l32, 2 * ks + g) : 0;
   }
 
+  const bool active = m0 + wm * (BM / WM) < p.M && n0 + wn * (BN / WN) < p.N;
   f32x16 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -219,6 +226,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);  // into the stage read at kt-1
     const uint16_t* at = st;
     const uint16_t* bt = st + TILE;
+    // a wave whose rows or columns all lie outside C skips its MFMAs (their
+    // results would not be stored)
+    if (active)
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       u32x4 a[MB], b[NB];
