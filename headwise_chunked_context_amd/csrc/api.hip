@@ -71,22 +71,23 @@ int check_shape(int64_t L, int32_t hidden, int32_t n_q, int32_t n_kv, int32_t he
 }
 
 // Split-K factor of the weight-gradient GEMMs (reduction over L).  The
-// 256 x 256 workgroups run one per CU, so the time of a split count s is
-// about ceil(tiles*s / 256) rounds of 1/s of the reduction each, plus a
-// small cost per split for the fp32 atomics of its epilogue (0.01 of the
-// unsplit time per split, fitted to measurements of the layer's two shapes).
-// Each split keeps at least 512 rows of the sequence.
+// 256 x 256 workgroups run one per CU, so with s splits the GEMM takes about
+// ceil(tiles*s / 256) rounds of ceil(L / (64 s)) k steps each, plus a fixed
+// cost per split for its fp32 atomic epilogue, about 5 k steps (fitted to
+// measurements of the layer's shapes).  Each split keeps at least 512 rows
+// of the sequence.
 int dw_splits(int64_t L, int M, int N) {
-  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   int max_s = (int)((L + 511) / 512);
   if (max_s > 32) max_s = 32;
   if (max_s < 1) max_s = 1;
   int best = 1;
-  double best_cost = 1e30;
+  int64_t best_cost = INT64_MAX;
   for (int sp = 1; sp <= max_s; ++sp) {
-    const double rounds = (double)((tiles * sp + 255) / 256);
-    const double cost = rounds / sp + 0.01 * sp;
-    if (cost < best_cost - 1e-12) {
+    const int64_t rounds = (tiles * sp + 255) / 256;
+    const int64_t steps = (L + 64LL * sp - 1) / (64LL * sp);
+    const int64_t cost = rounds * steps + 5LL * sp;
+    if (cost < best_cost) {
       best_cost = cost;
       best = sp;
     }
