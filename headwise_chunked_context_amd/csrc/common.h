@@ -38,6 +38,16 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies A row
+// (l % 16) and B column (l % 16), eight k values each (slot 8*(l/16) .. +7 of
+// the 32); the result element (row i, col j) sits in lane j + 16*(i/4),
+// register i % 4.  Same FLOPs per cycle as the 32x32x16 shape with half the
+// accumulator traffic per FLOP.
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // Same shape with fp16 operands (10-bit mantissa); used where bf16's 7 bits
 // cost too much accuracy (the probabilities and values of O = P V).
 __device__ __forceinline__ f32x16 mfma32_f16(const u32x4& a, const u32x4& b, const f32x16& c) {

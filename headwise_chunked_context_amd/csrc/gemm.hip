@@ -5,8 +5,11 @@
 //   NN  dy . W_o[:, cols], dqkv . W   (B n-contiguous)
 //   TN  dy^T . O, dqkv^T . x          (both m/n-contiguous; K = L, split-K)
 // Workgroup tile 256 x 256, k step 64, on 512 threads: 8 waves, two per
-// SIMD, each owning 128 x 64 of C as 4 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 128 registers).  (One wave
+// SIMD, each owning 128 x 64 of C as 8 x 4 blocks of
+// v_mfma_f32_16x16x32_bf16 (fp32 accumulators, 128 registers; the 16x16
+// shape moves half the accumulator data per FLOP of the 32x32x16 one, which
+// measured on par here: the GEMMs run near 2 GHz, below the power limit
+// that binds the attention kernels).  (One wave
 // per SIMD with 128 x 128 each halves the LDS reads per MFMA but measured
 // slower, with and without software-pipelined operand reads.)
 // Operand tiles go straight from global memory to LDS by asynchronous
@@ -34,8 +37,8 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int WM = 2, WN = 4;               // waves along M and N
 constexpr int NT = 64 * WM * WN;            // threads
-constexpr int MB = BM / WM / 32;            // 32x32 blocks per wave along M
-constexpr int NB = BN / WN / 32;            // ... along N
+constexpr int MB = BM / WM / 16;            // 16x16 blocks per wave along M
+constexpr int NB = BN / WN / 16;            // ... along N
 constexpr int STAGES = BK == 32 ? 4 : 2;   // 128 KB of LDS either way
 static_assert(WM == 2, "the bf16 epilogue stages one 128-row half of C per wave row");
 constexpr int TILE = 256 * BK;              // elements of one operand tile
@@ -52,6 +55,21 @@ __device__ __forceinline__ int kmaj_swz(int row) {
 }
 __device__ __forceinline__ int kmaj_off(int row, int chunk) {
   return row * BK + ((chunk ^ kmaj_swz(row)) << 3);
+}
+
+// 16x16x32 operand from an m/n-major tile (k down the rows, m/n along the
+// columns; the swizzled 256-byte-row layout of common.h): lane l gets
+// column m0 + l % 16 and rows k0 + 8*(l/16) .. +7.  Two transpose reads: in
+// each 16-lane group, lane p addresses row k0 + 8*(l/16) + p/4 (+4) and the
+// four columns m0 + 4*(p%4) .., so lane i receives column m0 + i.
+__device__ __forceinline__ u32x4 tile_read_t16(const uint16_t* tile, int k0, int m0, int lane) {
+  const int s = lane & 15;
+  const int col = m0 + 4 * (s & 3);
+  const int chunk = col >> 3, half = col & 7;
+  const int r0 = k0 + 8 * (lane >> 4) + (s >> 2);
+  u32x2 lo = lds_read_tr16(tile + tile_off(r0, chunk) + half);
+  u32x2 hi = lds_read_tr16(tile + tile_off(r0 + 4, chunk) + half);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
 __device__ __forceinline__ int64_t seg_map(const RowSegments& s, int idx) {
@@ -86,7 +104,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   // wave instead of two SIMDs keeping two
   static_assert(WM == 2 && WN == 4, "wave mapping below");
   const int wm = (wave >> 1) & 1, wn = (wave & 1) + 2 * (wave >> 2);
-  const int g = lane >> 5, l32 = lane & 31;
 
   // XCD-aware tile order: the dispatcher deals workgroups to the 8 XCDs
   // round-robin, so workgroup i runs on XCD i % 8.  Renumber so that each
@@ -183,19 +200,22 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   };
 
   // per-lane LDS element offsets of the MFMA operands within a stage
-  int aoff[BK / 16], boff[BK / 16];
+  //  (16x16x32 operands: row l % 16 of a 16-row block, k chunk 4ks + l/16;
+  //  16 rows further keep the swizzle, so blocks are an immediate apart)
+  const int l16 = lane & 15, q4 = lane >> 4;
+  int aoff[BK / 32], boff[BK / 32];
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    aoff[ks] = A_K ? kmaj_off(wm * (BM / WM) + l32, 2 * ks + g) : 0;
-    boff[ks] = B_K ? kmaj_off(wn * (BN / WN) + l32, 2 * ks + g) : 0;
+  for (int ks = 0; ks < BK / 32; ++ks) {
+    aoff[ks] = A_K ? kmaj_off(wm * (BM / WM) + l16, 4 * ks + q4) : 0;
+    boff[ks] = B_K ? kmaj_off(wn * (BN / WN) + l16, 4 * ks + q4) : 0;
   }
 
   const bool active = m0 + wm * (BM / WM) < p.M && n0 + wn * (BN / WN) < p.N;
-  f32x16 acc[MB][NB];
+  f32x4 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // prologue: three k steps in flight
 #pragma unroll
@@ -230,27 +250,27 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     // results would not be stored)
     if (active)
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < BK / 32; ++ks) {
       u32x4 a[MB], b[NB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         if (A_K)
-          a[mb] = *reinterpret_cast<const u32x4*>(at + aoff[ks] + mb * 32 * BK);
+          a[mb] = *reinterpret_cast<const u32x4*>(at + aoff[ks] + mb * 16 * BK);
         else
-          a[mb] = tile_read_t_nat(at + wm * HALF, ks * 16, mb * 32, lane);
+          a[mb] = tile_read_t16(at + wm * HALF, ks * 32, mb * 16, lane);
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int col = wn * (BN / WN) + nb * 32;
+        const int col = wn * (BN / WN) + nb * 16;
         if (B_K)
-          b[nb] = *reinterpret_cast<const u32x4*>(bt + boff[ks] + nb * 32 * BK);
+          b[nb] = *reinterpret_cast<const u32x4*>(bt + boff[ks] + nb * 16 * BK);
         else
-          b[nb] = tile_read_t_nat(bt + (col >> 7) * HALF, ks * 16, col & 127, lane);
+          b[nb] = tile_read_t16(bt + (col >> 7) * HALF, ks * 32, col & 127, lane);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(a[mb], b[nb], acc[mb][nb]);
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma16(a[mb], b[nb], acc[mb][nb]);
     }
   }
   __syncthreads();  // the epilogue reuses the stages
@@ -262,10 +282,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int n = n0 + wn * (BN / WN) + nb * 32 + l32;
+        const int n = n0 + wn * (BN / WN) + nb * 16 + l16;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * (BM / WM) + mb * 32 + acc_row(r, g);
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * (BM / WM) + mb * 16 + 4 * q4 + r;
           if (m < p.M && n < p.N) atomicAdd(C + (int64_t)m * p.N + n, acc[mb][nb][r]);
         }
       }
@@ -298,8 +318,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            Cs[(mb * 32 + acc_row(r, g)) * BN + wn * (BN / WN) + nb * 32 + l32] = acc[mb][nb][r];
+          for (int r = 0; r < 4; ++r)
+            Cs[(mb * 16 + 4 * q4 + r) * BN + wn * (BN / WN) + nb * 16 + l16] = acc[mb][nb][r];
     }
     __syncthreads();
 #pragma unroll
