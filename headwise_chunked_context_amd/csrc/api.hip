@@ -222,10 +222,23 @@ template <typename F>
 hipError_t timed(int kind, hipStream_t st, F&& launch) {
   if (!g_prof.on) return launch();
   hipEvent_t a = prof_event(), b = prof_event();
-  if (!a || !b) return hipErrorOutOfMemory;
-  if (hipEventRecord(a, st) != hipSuccess) return hipErrorUnknown;
+  auto give_back = [&]() {  // events of a failed bracket return to the pool
+    if (a) g_prof.pool.push_back(a);
+    if (b) g_prof.pool.push_back(b);
+  };
+  if (!a || !b) {
+    give_back();
+    return hipErrorOutOfMemory;
+  }
+  if (hipEventRecord(a, st) != hipSuccess) {
+    give_back();
+    return hipErrorUnknown;
+  }
   hipError_t e = launch();
-  if (hipEventRecord(b, st) != hipSuccess) return hipErrorUnknown;
+  if (hipEventRecord(b, st) != hipSuccess) {
+    give_back();
+    return hipErrorUnknown;
+  }
   g_prof.rec[kind].push_back({a, b});
   return e;
 }
@@ -254,13 +267,22 @@ int side_stream(Side** out) {
   std::lock_guard<std::mutex> lock(g_side_mu);
   Side& sd = g_side[dev];
   if (!sd.stream) {
-    hipEvent_t* evs[5] = {&sd.fork, &sd.ready[0], &sd.ready[1], &sd.done[0], &sd.done[1]};
+    // created into a local copy and published only when everything exists,
+    // so a failed attempt leaves nothing behind and the next call retries
+    Side fresh;
+    hipEvent_t* evs[5] = {&fresh.fork, &fresh.ready[0], &fresh.ready[1], &fresh.done[0],
+                          &fresh.done[1]};
+    bool ok = true;
     for (hipEvent_t* e : evs)
-      if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) return UPIPE_EHIP;
-    if (hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking) != hipSuccess) {
-      sd.stream = nullptr;
+      ok = ok && hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipStreamCreateWithFlags(&fresh.stream, hipStreamNonBlocking) == hipSuccess;
+    if (!ok) {
+      for (hipEvent_t* e : evs)
+        if (*e) (void)hipEventDestroy(*e);
+      if (fresh.stream) (void)hipStreamDestroy(fresh.stream);
       return UPIPE_EHIP;
     }
+    sd = fresh;
   }
   *out = &sd;
   return UPIPE_OK;
