@@ -135,6 +135,41 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check(t, name: str, shape: tuple, dtype, device=None):
+    """The library sees only a pointer: the tensor must be a contiguous
+    device tensor of exactly this shape and dtype (a wrong extent would make
+    the kernels read or write outside it)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on the GPU device of x")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_inputs(x, w_qkv, w_o, n_q: int, n_kv: int, head_dim: int):
+    import torch
+
+    bf = torch.bfloat16
+    if x is None or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor")
+    L = x.shape[0]
+    if (w_qkv is None) != (w_o is None):
+        raise ValueError("w_qkv and w_o are given together (projection mode) or not at all")
+    if w_qkv is not None:
+        hidden = x.shape[1]
+        _check(x, "x", (L, hidden), bf)
+        _check(w_qkv, "w_qkv", ((n_q + 2 * n_kv) * head_dim, hidden), bf, x.device)
+        _check(w_o, "w_o", (hidden, n_q * head_dim), bf, x.device)
+    else:
+        _check(x, "x (packed q|k|v)", (L, (n_q + 2 * n_kv) * head_dim), bf)
+    return L
+
+
 def _stream(stream):
     import torch
 
@@ -146,6 +181,8 @@ def _workspace(nbytes: int, device, workspace):
     import torch
 
     if workspace is not None:
+        if not workspace.is_cuda or workspace.device != device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the device of x")
         return workspace
     # 256-byte aligned by the caching allocator
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -160,7 +197,7 @@ def attn_fwd(x, w_qkv, w_o, n_q: int, n_kv: int, head_chunk: int, theta: float,
     """
     import torch
 
-    L = x.shape[0]
+    L = _check_inputs(x, w_qkv, w_o, n_q, n_kv, head_dim)
     proj = w_qkv is not None
     hidden = x.shape[1] if proj else 0
     dev = x.device
@@ -184,10 +221,14 @@ def attn_bwd(x, w_qkv, w_o, o_saved, lse, dy, n_q: int, n_kv: int, head_chunk: i
     (projection mode only) each chunk's attention output is recomputed."""
     import torch
 
-    L = x.shape[0]
+    L = _check_inputs(x, w_qkv, w_o, n_q, n_kv, head_dim)
     proj = w_qkv is not None
     hidden = x.shape[1] if proj else 0
     dev = x.device
+    if o_saved is not None:
+        _check(o_saved, "o_saved", (L, n_q * head_dim), torch.bfloat16, dev)
+    _check(lse, "lse", (n_q, L), torch.float32, dev)
+    _check(dy, "dy", (L, hidden if proj else n_q * head_dim), torch.bfloat16, dev)
     dx = torch.empty_like(x)
     dw_qkv = torch.empty_like(w_qkv) if proj else None
     dw_o = torch.empty_like(w_o) if proj else None

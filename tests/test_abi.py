@@ -231,3 +231,17 @@ def test_pipelined_forward_workspace_and_check():
         hc_amd.pipeline_enable(False)
     assert hc_amd.fwd_pass() == B.PASS_FWD
     assert _fwd(L=L, wsb=one - 1) == B.UPIPE_EWORKSPACE
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    """The binding validates tensors before it reaches the library: host
+    tensors are refused (no pointer of them ever reaches a kernel)."""
+    import torch
+
+    x = torch.zeros(16, 128, dtype=torch.bfloat16)
+    wq = torch.zeros(3 * 128, 128, dtype=torch.bfloat16)
+    wo = torch.zeros(128, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        hc_amd.attn_fwd(x, wq, wo, 1, 1, 1, 5e5)
+    with pytest.raises(ValueError):
+        hc_amd.attn_fwd(x, wq, None, 1, 1, 1, 5e5)   # weights come together
