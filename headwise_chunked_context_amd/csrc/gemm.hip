@@ -13,15 +13,14 @@
 // per SIMD with 128 x 128 each halves the LDS reads per MFMA but measured
 // slower, with and without software-pipelined operand reads.)
 // Operand tiles go straight from global memory to LDS by asynchronous
-// global->LDS copies into two LDS stages of 64 KB.  With a k-contiguous
-// operand (NT, NN) each wave holds one k half of operand fragments in
-// registers while it reads the next, and the one barrier per step sits
-// between the two halves' MFMAs: the copy of step t+2 is issued there and
-// lands within a step, and the MFMAs after the barrier start from registers
-// (3% less GEMM time than a barrier in front of each step's first reads).
-// TN keeps the barrier in front of each step: its transpose-read addresses
-// leave no registers for a second set of fragments.  (A k step of 32 with
-// four stages measured 4% slower: twice the barriers and operand-read
+// global->LDS copies into two LDS stages of 64 KB.  Each wave holds one k
+// half of operand fragments in registers while it reads the next, and the
+// one barrier per step sits between the two halves' MFMAs: the copy of step
+// t+2 is issued there and lands within a step, and the MFMAs after the
+// barrier start from registers (3% less GEMM time for NT/NN, and 3% more
+// once TN's transpose-read addresses, XORed from one base per operand,
+// left it the registers for the second set of fragments).  (A k step of 32
+// with four stages measured 4% slower: twice the barriers and operand-read
 // latency bubbles per MFMA.)  The copies stage the tiles as they lie in
 // memory, no transposing stores:
 //  * a k-contiguous operand is [256 rows][64 k] with 128-byte rows and the
@@ -51,6 +50,8 @@ constexpr int HALF = 128 * BK;              // one [BK][128] half of an m/n-majo
 constexpr int CHUNKS = BK / 8;              // 16-byte chunks per k-major row
 constexpr int ROWS_PER_KB = 512 / BK;       // k-major rows per 1 KB copy block
 constexpr int STAGE = 2 * TILE;             // A and B tiles of one k step
+static_assert((2 * HALF) % 256 == 0 && (2 * TILE) % 256 == 0 && (2 * STAGE) % 256 == 0,
+              "tile bases keep the low 8 LDS address bits clear");
 
 // k-major tile: rows of BK elements, the 16-byte chunk index XORed so that
 // 16 lanes reading 16 consecutive rows at one chunk hit distinct banks
@@ -67,13 +68,29 @@ __device__ __forceinline__ int kmaj_off(int row, int chunk) {
 // column m0 + l % 16 and rows k0 + 8*(l/16) .. +7.  Two transpose reads: in
 // each 16-lane group, lane p addresses row k0 + 8*(l/16) + p/4 (+4) and the
 // four columns m0 + 4*(p%4) .., so lane i receives column m0 + i.
-__device__ __forceinline__ u32x4 tile_read_t16(const uint16_t* tile, int k0, int m0, int lane) {
+// The addresses keep two registers per operand instead of two per column
+// block.  In the swizzled layout the byte
+// address of (row r, column 16j + 4(s%4)) is r*256 + 8*(s%2) + 16*(c ^ swz(r))
+// with c = 2j + (s%4)/2; j only enters through bits 5..7, so for a tile at a
+// 256-byte aligned address, column block j's address is block 0's XOR (j << 5).
+// tr16_base gives block 0's addresses of the lo (k0 + 8*(l/16) + p/4) and hi
+// (+4) rows; 32 more k rows are +8192 bytes (the swizzle repeats every 16 rows).
+__device__ __forceinline__ u32x2 tr16_base(uint32_t tile, int lane) {
   const int s = lane & 15;
-  const int col = m0 + 4 * (s & 3);
-  const int chunk = col >> 3, half = col & 7;
-  const int r0 = k0 + 8 * (lane >> 4) + (s >> 2);
-  u32x2 lo = lds_read_tr16(tile + tile_off(r0, chunk) + half);
-  u32x2 hi = lds_read_tr16(tile + tile_off(r0 + 4, chunk) + half);
+  const int c0 = (s & 3) >> 1, half = 4 * (s & 1);
+  const int r0 = 8 * (lane >> 4) + (s >> 2);
+  return u32x2{tile + 2u * (uint32_t)(tile_off(r0, c0) + half),
+               tile + 2u * (uint32_t)(tile_off(r0 + 4, c0) + half)};
+}
+__device__ __forceinline__ u32x2 lds_tr16_at(uint32_t addr) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+// column block j at k rows 32*ks .. of a tile whose block-0 addresses are b
+__device__ __forceinline__ u32x4 tr16_read(u32x2 b, int j, int ks) {
+  const u32x2 lo = lds_tr16_at((b[0] ^ (uint32_t)(j << 5)) + 8192u * ks);
+  const u32x2 hi = lds_tr16_at((b[1] ^ (uint32_t)(j << 5)) + 8192u * ks);
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -97,7 +114,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <bool A_K, bool B_K, int EPI>
 __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * STAGE];  // 128 KB
+  // 256-byte aligned: the transpose-read addresses below rely on it
+  __shared__ __attribute__((aligned(256))) uint16_t smem[STAGES * STAGE];  // 128 KB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,136 +240,105 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (!A_K && !B_K) {
-    // both operands m/n-major (transpose reads; split-K, ragged last step):
-    // one barrier per k step, fragments read at the start of each k half
+  // The two k halves of a step are read into separate registers, and the
+  // barrier sits between the halves' MFMAs instead of in front of a step's
+  // first reads:
+  //   [MFMAs of half 0 | reads of half 1]  wait, barrier, copy of kt+2
+  //   [MFMAs of half 1 | reads of half 0 of step kt+1]
+  // At the barrier every wave has all of step kt in registers (its stage
+  // may be refilled) and step kt+1 has landed, so the MFMAs after the
+  // barrier start from registers while the next step's first reads are in
+  // flight.
+  static_assert(STAGES == 2 && BK == 64, "two stages of two k halves");
+  constexpr int RD = (A_K ? MB : 2 * MB) + (B_K ? NB : 2 * NB);  // LDS reads per k half
+  constexpr int MPR = (MB * NB) / RD;                             // MFMAs per read
+  static_assert(MPR >= 1, "interleave");
+  u32x4 a0[MB], b0[NB], a1[MB], b1[NB];
+  // block-0 transpose-read addresses of stage 0 (m/n-major operands)
+  const u32x2 atr = tr16_base(lds_addr(smem) + 2u * (uint32_t)(wm * HALF), lane);
+  const u32x2 btr = tr16_base(lds_addr(smem) + 2u * (uint32_t)(TILE + (wn >> 1) * HALF), lane);
+  auto frags = [&](int stage, int ks, u32x4* af, u32x4* bf) __attribute__((always_inline)) {
+    const uint16_t* at = smem + stage * STAGE;
+    const uint16_t* bt = at + TILE;
+    const uint32_t so = 2u * (uint32_t)(stage * STAGE);
 #pragma unroll
-    for (int t = 0; t < STAGES - 1; ++t)
-      if (t < nk) issue(t);
+    for (int nb = 0; nb < NB; ++nb) {
+      if (B_K)
+        bf[nb] = *reinterpret_cast<const u32x4*>(bt + boff[ks] + nb * 16 * BK);
+      else
+        bf[nb] = tr16_read(u32x2{btr[0] + so, btr[1] + so}, 4 * (wn & 1) + nb, ks);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (A_K)
+        af[mb] = *reinterpret_cast<const u32x4*>(at + aoff[ks] + mb * 16 * BK);
+      else
+        af[mb] = tr16_read(u32x2{atr[0] + so, atr[1] + so}, mb, ks);
+    }
+  };
+  auto mfmas = [&](const u32x4* af, const u32x4* bf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma16(af[mb], bf[nb], acc[mb][nb]);
+  };
+  // MFMAs of one half with the RD reads of the other between them
+  auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < RD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - RD * MPR, 0);
+  };
+  // An m/n-major A read k rows past the end of the split clamped: once step
+  // kt has landed, its rows past the end are zeroed (a uniform branch taken
+  // by every wave, active or not, with the barrier that publishes the zeros)
+  auto zero_tail = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kbeg + kt * BK;
+    if (A_K || k0 + BK <= kend) return;
+    uint16_t* st = smem + (kt & 1) * STAGE;
+    const int valid = kend - k0;
+    for (int c = tid; c < BK * 32; c += NT) {
+      const int row = c >> 5;
+      if (row >= valid)
+        *reinterpret_cast<u32x4*>(st + (c & 16 ? HALF : 0) + row * 128 + (c & 15) * 8) = u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+  };
 
+  issue(0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  zero_tail(0);
+  if (nk > 1) issue(1);
+  if (active) {
+    frags(0, 0, a0, b0);
     for (int kt = 0; kt < nk; ++kt) {
-      // this wave's copies of step kt are done once at most the copies of the
-      // (up to two) later steps already issued are outstanding
-      constexpr int PER = 2 * CPW;  // copies per wave per k step
-      const int later = min(nk - 1 - kt, STAGES - 2);
-      if (later >= 2) wait_vmcnt<2 * PER>();
-      else if (later == 1) wait_vmcnt<PER>();
-      else wait_vmcnt<0>();
-      __syncthreads();  // every wave's copies of step kt landed; step kt-1 fully read
-      const int k0 = kbeg + kt * BK;
-      uint16_t* st = smem + (kt % STAGES) * STAGE;
-      if (k0 + BK > kend) {
-        // k rows past the end of the split were read clamped: zero them in A
-        const int valid = kend - k0;
-        for (int c = tid; c < BK * 32; c += NT) {
-          const int row = c >> 5;
-          if (row >= valid)
-            *reinterpret_cast<u32x4*>(st + (c & 16 ? HALF : 0) + row * 128 + (c & 15) * 8) = u32x4{0, 0, 0, 0};
-        }
-        __syncthreads();
-      }
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);  // into the stage read at kt-1
-      const uint16_t* at = st;
-      const uint16_t* bt = st + TILE;
-      // a wave whose rows or columns all lie outside C skips its MFMAs (their
-      // results would not be stored)
-      if (active)
-#pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) {
-        u32x4 a[MB], b[NB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) a[mb] = tile_read_t16(at + wm * HALF, ks * 32, mb * 16, lane);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int col = wn * (BN / WN) + nb * 16;
-          b[nb] = tile_read_t16(bt + (col >> 7) * HALF, ks * 32, col & 127, lane);
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma16(a[mb], b[nb], acc[mb][nb]);
-      }
+      frags(kt & 1, 1, a1, b1);
+      mfmas(a0, b0);
+      interleave();
+      // this wave's reads of the stage have returned; the copies of step
+      // kt+1 (the only ones in flight) have landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      if (kt + 1 < nk) wait_vmcnt<0>();
+      __syncthreads();
+      if (kt + 1 < nk) zero_tail(kt + 1);
+      if (kt + 2 < nk) issue(kt + 2);  // into the stage just released
+      // (after the last step these reads are unused: the stage they read
+      // is a valid one that nothing writes any more)
+      frags((kt + 1) & 1, 0, a0, b0);
+      mfmas(a1, b1);
+      interleave();
     }
   } else {
-    // at least one k-contiguous operand (K a multiple of BK: no ragged step).
-    // The two k halves of a step are read into separate registers, and the
-    // barrier sits between the halves' MFMAs instead of in front of a step's
-    // first reads:
-    //   [MFMAs of half 0 | reads of half 1]  wait, barrier, copy of kt+2
-    //   [MFMAs of half 1 | reads of half 0 of step kt+1]
-    // At the barrier every wave has all of step kt in registers (its stage
-    // may be refilled) and step kt+1 has landed, so the MFMAs after the
-    // barrier start from registers while the next step's first reads are in
-    // flight.
-    static_assert(STAGES == 2 && BK == 64, "two stages of two k halves");
-    constexpr int RD = (A_K ? MB : 2 * MB) + (B_K ? NB : 2 * NB);  // LDS reads per k half
-    constexpr int MPR = (MB * NB) / RD;                             // MFMAs per read
-    static_assert(MPR >= 1, "interleave");
-    u32x4 a0[MB], b0[NB], a1[MB], b1[NB];
-    auto frags = [&](const uint16_t* st, int ks, u32x4* af, u32x4* bf) __attribute__((always_inline)) {
-      const uint16_t* at = st;
-      const uint16_t* bt = st + TILE;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int col = wn * (BN / WN) + nb * 16;
-        if (B_K)
-          bf[nb] = *reinterpret_cast<const u32x4*>(bt + boff[ks] + nb * 16 * BK);
-        else
-          bf[nb] = tile_read_t16(bt + (col >> 7) * HALF, ks * 32, col & 127, lane);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if (A_K)
-          af[mb] = *reinterpret_cast<const u32x4*>(at + aoff[ks] + mb * 16 * BK);
-        else
-          af[mb] = tile_read_t16(at + wm * HALF, ks * 32, mb * 16, lane);
-      }
-    };
-    auto mfmas = [&](const u32x4* af, const u32x4* bf) __attribute__((always_inline)) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma16(af[mb], bf[nb], acc[mb][nb]);
-    };
-    // MFMAs of one half with the RD reads of the other between them
-    auto interleave = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < RD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - RD * MPR, 0);
-    };
-
-    issue(0);
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (nk > 1) issue(1);
-    if (active) {
-      frags(smem, 0, a0, b0);
-      for (int kt = 0; kt < nk; ++kt) {
-        frags(smem + (kt & 1) * STAGE, 1, a1, b1);
-        mfmas(a0, b0);
-        interleave();
-        // this wave's reads of the stage have returned; the copies of step
-        // kt+1 (the only ones in flight) have landed
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        if (kt + 1 < nk) wait_vmcnt<0>();
-        __syncthreads();
-        if (kt + 2 < nk) issue(kt + 2);  // into the stage just released
-        // (after the last step these reads are unused: the stage they read
-        // is a valid one that nothing writes any more)
-        frags(smem + ((kt + 1) & 1) * STAGE, 0, a0, b0);
-        mfmas(a1, b1);
-        interleave();
-      }
-    } else {
-      // no MFMAs, the same copies and barriers
-      for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) wait_vmcnt<0>();
-        __syncthreads();
-        if (kt + 2 < nk) issue(kt + 2);
-      }
+    // a wave whose rows or columns all lie outside C skips its reads and
+    // MFMAs (their results would not be stored), not the copies and barriers
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) wait_vmcnt<0>();
+      __syncthreads();
+      if (kt + 1 < nk) zero_tail(kt + 1);
+      if (kt + 2 < nk) issue(kt + 2);
     }
   }
   __syncthreads();  // the epilogue reuses the stages
