@@ -307,7 +307,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     __syncthreads();
   };
 
-  issue(0);
+  // (the launcher sizes the grid so every split has at least one k step;
+  // the guard keeps an empty one from copying past its end regardless)
+  if (nk > 0) issue(0);
   wait_vmcnt<0>();
   __syncthreads();
   zero_tail(0);
