@@ -44,7 +44,7 @@ CPU_SAMPLE_L = 8192
 KERNEL_SOURCES = {
     "attn_fwd": "headwise_chunked_context_amd/csrc/flash_fwd.hip",
     "attn_bwd_dkdv": "headwise_chunked_context_amd/csrc/flash_bwd.hip",
-    "attn_bwd_dq": "headwise_chunked_context_amd/csrc/flash_bwd.hip",
+    "attn_bwd_dq": "headwise_chunked_context_amd/csrc/flash_bwd_dq.hip",
     "gemm": "headwise_chunked_context_amd/csrc/gemm.hip",
     "prep": "headwise_chunked_context_amd/csrc/prep.hip",
 }

@@ -36,6 +36,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-file additions.  The dQ kernel's own file takes LLVM's max-ILP machine
+# scheduler: measured 2.5% faster for that kernel than the default strategy,
+# which stays for the others (the dK/dV kernel measured 3% slower with it).
+FILE_FLAGS = {
+    "flash_bwd_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -54,7 +62,7 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(OBJ, os.path.basename(src).replace(".hip", ".o"))
-        cmd = [hipcc, *flags, "-c", src, "-o", obj]
+        cmd = [hipcc, *flags, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         out = (res.stdout + res.stderr).strip()
         # the host pass does not know the packed-fp32 feature name; harmless
