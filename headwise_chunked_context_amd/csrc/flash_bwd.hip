@@ -185,6 +185,9 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
       sv = mfma32(*reinterpret_cast<const u32x4*>(Qt + offq[ks]), lds_load16(ka, 0), sv);
       dp = mfma32(*reinterpret_cast<const u32x4*>(Ot + offq[ks]), vreg[ks], dp);
     }
+    // LLVM's LDS-read / MFMA interleave strategy for this block: measured 1%
+    // faster; the same hint on the dV/dK block below was 4% slower
+    __builtin_amdgcn_iglp_opt(0);
     if (need_mask) {  // key after the query, or a padding query row
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
