@@ -229,6 +229,16 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
         const u32x2 q_hi = lds_read_tr16(Qt + offt[db][1] + h * 2048);
         acc_dk[db] = mfma32(u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}, pS[h], acc_dk[db]);
       }
+    // transpose reads kept eight (four MFMAs) ahead, then two per MFMA:
+    // measured 1% faster than the compiler's order (LLVM's generic LDS/MFMA
+    // interleave here was 4% slower)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_s_setprio(0);
   };
 
