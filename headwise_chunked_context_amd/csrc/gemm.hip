@@ -329,9 +329,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
       if (kt + 2 < nk) issue(kt + 2);  // into the stage just released
       // (after the last step these reads are unused: the stage they read
       // is a valid one that nothing writes any more)
+      // the half after the barrier issues at raised wave priority
+      // (measured 0.6% less GEMM time; raising the first half: no change)
+      __builtin_amdgcn_s_setprio(1);
       frags((kt + 1) & 1, 0, a0, b0);
       mfmas(a1, b1);
       interleave();
+      __builtin_amdgcn_s_setprio(0);
     }
   } else {
     // a wave whose rows or columns all lie outside C skips its reads and
