@@ -15,10 +15,13 @@ value = model FLOPs per step / time per step, with
               + 6 L Hq d hidden             (output projection fwd + dO + dW)
 Recomputation inside the backward is executed but not counted.
 
-roofline: the kernel class with the largest GPU time in the timed region,
-timed live with HIP events the library records around each of its launches on
-the launch stream; achieved = its algorithmic FLOPs per launch / its average
-launch duration.  traffic comes from profiles/traffic_*.json (rocprofv3 PMC
+roofline: the kernel class with the largest GPU time (found on the last
+warm-up step, which times every class; that step also gives
+kernel_breakdown and the attn_*_tflops figures), timed live over the timed
+steps with HIP events the library records around each of its launches on the
+launch stream, and around no other launch (events around every launch
+cost about 1% of a step); achieved = its algorithmic FLOPs per launch / its
+average launch duration.  traffic comes from profiles/traffic_*.json (rocprofv3 PMC
 counters scaled by a copy-kernel calibration) when that file's kernel source
 hash matches the current source, else null.
 
@@ -191,12 +194,27 @@ def main() -> int:
         lib.attn_bwd(x, wq, wo, None if args.recompute else o, lse, dy, w.n_q, w.n_kv, hc, w.theta,
                      workspace=ws)
 
-    for _ in range(args.warmup):
+    # The last warm-up step times every kernel class (the breakdown, and which
+    # class dominates); the timed steps bracket only the dominant class's
+    # launches with events, since events around every launch cost ~1% of a
+    # step.  With no warm-up the timed steps bracket every class.
+    prof_all = None
+    for i in range(args.warmup):
+        if i == args.warmup - 1:
+            torch.cuda.synchronize()
+            lib.profile_enable(True)
         step()
     torch.cuda.synchronize()
+    if args.warmup > 0:
+        prof_all = lib.profile_read()
+        lib.profile_enable(False)
     mem0 = torch.cuda.max_memory_allocated(dev)
 
-    lib.profile_enable(True)
+    classes = ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm")
+    dom = None
+    if prof_all is not None:
+        dom = max((k for k in classes if prof_all[k][1] > 0), key=lambda k: prof_all[k][0])
+    lib.profile_enable(True, kinds=None if dom is None else [dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -205,6 +223,10 @@ def main() -> int:
     t1 = time.perf_counter()
     prof = lib.profile_read()
     lib.profile_enable(False)
+    prof_steps = 1
+    if prof_all is None:
+        prof_all, prof_steps = prof, args.steps
+        dom = max((k for k in classes if prof[k][1] > 0), key=lambda k: prof[k][0])
 
     ms = (t1 - t0) * 1e3 / args.steps
     flops = model_flops(w)
@@ -224,8 +246,6 @@ def main() -> int:
         "attn_bwd_dkdv": 8.0 * d * P * hc,
         "attn_bwd_dq": 2.0 * d * P * hc,
     }
-    kinds = [k for k in ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm") if prof[k][1] > 0]
-    dom = max(kinds, key=lambda k: prof[k][0])
     tot_ms, launches = prof[dom]
     avg_ms = tot_ms / launches
     if dom == "gemm":
@@ -244,16 +264,17 @@ def main() -> int:
         "avg_launch_ms": round(avg_ms, 4),
         "launches": launches,
     }
-    # the whole attention backward (both kernels) against its 10 d P hc
-    nb = prof["attn_bwd_dkdv"][1]
+    # the whole attention backward (both kernels) against its 10 d P hc, and
+    # the forward, from the step that timed every class
+    nb = prof_all["attn_bwd_dkdv"][1]
     if nb:
-        bwd_ms = (prof["attn_bwd_dkdv"][0] + prof["attn_bwd_dq"][0]) / nb
+        bwd_ms = (prof_all["attn_bwd_dkdv"][0] + prof_all["attn_bwd_dq"][0]) / nb
         roofline["attn_bwd_tflops"] = round(10.0 * d * P * hc / (bwd_ms * 1e-3) / 1e12, 2)
-    nf = prof["attn_fwd"][1]
+    nf = prof_all["attn_fwd"][1]
     if nf:
-        roofline["attn_fwd_tflops"] = round(algo["attn_fwd"] / (prof["attn_fwd"][0] / nf * 1e-3) / 1e12, 2)
-    breakdown = {k: {"ms_per_step": round(v[0] / args.steps, 3), "launches_per_step": v[1] // max(1, args.steps)}
-                 for k, v in prof.items()}
+        roofline["attn_fwd_tflops"] = round(algo["attn_fwd"] / (prof_all["attn_fwd"][0] / nf * 1e-3) / 1e12, 2)
+    breakdown = {k: {"ms_per_step": round(v[0] / prof_steps, 3), "launches_per_step": v[1] // prof_steps}
+                 for k, v in prof_all.items()}
 
     chunks = [c for c in range(1, w.n_q + 1)
               if w.n_q % c == 0 and (c % (w.n_q // w.n_kv) == 0 or (w.n_q // w.n_kv) % c == 0)]

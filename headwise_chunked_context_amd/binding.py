@@ -114,9 +114,23 @@ def fwd_pass() -> int:
     return PASS_FWD_PIPELINED if _pipeline else PASS_FWD
 
 
-def profile_enable(on: bool) -> None:
-    """Start (clearing old records) or stop per-kernel-class event timing."""
-    lib().upipe_profile_enable(1 if on else 0)
+PROFILE_ALL = 0x3F
+
+
+def profile_enable(on: bool, kinds=None) -> None:
+    """Start (clearing old records) or stop per-kernel-class event timing.
+    kinds: the KERNEL_KINDS names whose launches are bracketed (default: all)."""
+    if not on:
+        mask = 0
+    elif kinds is None:
+        mask = PROFILE_ALL
+    else:
+        mask = 0
+        for k in kinds:
+            mask |= 1 << KERNEL_KINDS[k]
+    rc = lib().upipe_profile_enable(mask)
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_profile_enable")
 
 
 def profile_read() -> dict:

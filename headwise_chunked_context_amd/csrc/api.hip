@@ -201,7 +201,7 @@ int check_common(const Shape& s, double theta, const void* x, const void* w_qkv,
 // ---- optional per-kernel-class timing (see upipe_profile_enable)
 constexpr int kKinds = 6;
 struct Profiler {
-  bool on = false;
+  int mask = 0;  // bit k: launches of kernel class k are bracketed
   std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[kKinds];
   std::vector<hipEvent_t> pool;
 };
@@ -220,7 +220,7 @@ hipEvent_t prof_event() {
 
 template <typename F>
 hipError_t timed(int kind, hipStream_t st, F&& launch) {
-  if (!g_prof.on) return launch();
+  if (!((g_prof.mask >> kind) & 1)) return launch();
   hipEvent_t a = prof_event(), b = prof_event();
   auto give_back = [&]() {  // events of a failed bracket return to the pool
     if (a) g_prof.pool.push_back(a);
@@ -351,7 +351,8 @@ int upipe_pipeline_enable(int on) {
   return UPIPE_OK;
 }
 
-int upipe_profile_enable(int on) {
+int upipe_profile_enable(int mask) {
+  if (mask < 0 || mask > UPIPE_PROFILE_ALL) return UPIPE_EINVAL;
   for (int k = 0; k < kKinds; ++k) {
     for (auto& pr : g_prof.rec[k]) {
       g_prof.pool.push_back(pr.first);
@@ -359,7 +360,7 @@ int upipe_profile_enable(int on) {
     }
     g_prof.rec[k].clear();
   }
-  g_prof.on = on != 0;
+  g_prof.mask = mask;
   return UPIPE_OK;
 }
 

@@ -155,11 +155,15 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
 
 /*
  * Kernel timing for measurement tools (not needed to use the layer).
- * upipe_profile_enable(1) clears previous records and, until
- * upipe_profile_enable(0), brackets every kernel launch of upipe_attn_fwd /
- * upipe_attn_bwd with a pair of HIP events recorded on the caller's stream.
- * upipe_profile_read(kind, ...) waits for the recorded events and returns the
- * summed GPU milliseconds and the number of launches of one kernel class:
+ * upipe_profile_enable(mask) clears previous records and, until
+ * upipe_profile_enable(0), brackets each kernel launch of upipe_attn_fwd /
+ * upipe_attn_bwd whose class bit (1 << kind) is set in mask with a pair of
+ * HIP events recorded on the caller's stream (UPIPE_PROFILE_ALL: every
+ * class).  Each bracket adds two event records to the stream; bracketing
+ * every launch of a layer step costs about 1% of its time, one class a
+ * fraction of that.  upipe_profile_read(kind, ...) waits for the recorded
+ * events and returns the summed GPU milliseconds and the number of launches
+ * of one kernel class:
  *   UPIPE_KERNEL_ATTN_FWD      causal attention forward
  *   UPIPE_KERNEL_ATTN_BWD_DKDV causal attention backward, dK and dV
  *   UPIPE_KERNEL_ATTN_BWD_DQ   causal attention backward, dQ
@@ -168,7 +172,8 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
  *   UPIPE_KERNEL_FINALIZE      accumulator conversion, fills
  * State is process-wide and not thread-safe.  Events are host-side HIP
  * objects; no device memory is allocated.  Returns UPIPE_OK, UPIPE_EINVAL
- * (bad kind or NULL output) or UPIPE_EHIP.
+ * (a mask outside 0 .. UPIPE_PROFILE_ALL, a bad kind or NULL output) or
+ * UPIPE_EHIP.
  */
 #define UPIPE_KERNEL_ATTN_FWD 0
 #define UPIPE_KERNEL_ATTN_BWD_DKDV 1
@@ -176,7 +181,8 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
 #define UPIPE_KERNEL_GEMM 3
 #define UPIPE_KERNEL_PREP 4
 #define UPIPE_KERNEL_FINALIZE 5
-int upipe_profile_enable(int on);
+#define UPIPE_PROFILE_ALL 0x3F
+int upipe_profile_enable(int mask);
 int upipe_profile_read(int kind, double* total_ms, int64_t* launches);
 
 /*

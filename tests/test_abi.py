@@ -245,3 +245,18 @@ def test_binding_refuses_host_tensors_before_any_call():
         hc_amd.attn_fwd(x, wq, wo, 1, 1, 1, 5e5)
     with pytest.raises(ValueError):
         hc_amd.attn_fwd(x, wq, None, 1, 1, 1, 5e5)   # weights come together
+
+
+def test_profile_mask_bounds():
+    """upipe_profile_enable takes a class mask in 0 .. UPIPE_PROFILE_ALL and
+    refuses anything else; reading a class outside the six is refused too
+    (host-side state only, no GPU needed)."""
+    L = B.lib()
+    assert L.upipe_profile_enable(-1) == B.UPIPE_EINVAL
+    assert L.upipe_profile_enable(B.PROFILE_ALL + 1) == B.UPIPE_EINVAL
+    assert L.upipe_profile_enable(1 << B.KERNEL_KINDS["attn_bwd_dkdv"]) == B.UPIPE_OK
+    ms, n = ctypes.c_double(-1), ctypes.c_int64(-1)
+    assert L.upipe_profile_read(6, ctypes.byref(ms), ctypes.byref(n)) == B.UPIPE_EINVAL
+    assert L.upipe_profile_read(1, ctypes.byref(ms), ctypes.byref(n)) == B.UPIPE_OK
+    assert (ms.value, n.value) == (0.0, 0)
+    assert L.upipe_profile_enable(0) == B.UPIPE_OK
