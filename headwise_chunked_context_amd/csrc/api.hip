@@ -200,6 +200,7 @@ int check_common(const Shape& s, double theta, const void* x, const void* w_qkv,
 
 // ---- optional per-kernel-class timing (see upipe_profile_enable)
 constexpr int kKinds = 6;
+static_assert(UPIPE_PROFILE_ALL == (1 << kKinds) - 1, "one mask bit per kernel class");
 struct Profiler {
   int mask = 0;  // bit k: launches of kernel class k are bracketed
   std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[kKinds];
