@@ -307,10 +307,15 @@ Chunk chunk_info(const Shape& s, int c) {
   return ch;
 }
 
-// Stage the chunk's q (and k, v when it starts a group) in GEMM output
-// layout: staging[L][hc*d | kc*d | kc*d].
+// Project the chunk's q (and k, v when it starts a group).  q and k leave
+// the GEMM rotated and head-major, straight in q_rm / k_rm ([head][Lp][d],
+// all Lp rows: the padding rows L .. Lp-1 repeat x's last row, rotated at
+// their own positions, finite values that every attention kernel masks); v
+// goes to staging[L][hc*d | kc*d | kc*d] at its columns, for the layout
+// pass.
 int project_chunk(const Shape& s, const Chunk& ch, const uint16_t* x, const uint16_t* w_qkv,
-                  uint16_t* staging, const RopeTable& rope, hipStream_t st) {
+                  uint16_t* staging, uint16_t* q_rm, uint16_t* k_rm, const RopeTable& rope,
+                  hipStream_t st) {
   const int d = s.d;
   const int width = (s.hc + 2 * s.kc) * d;
   GemmArgs g;
@@ -328,10 +333,16 @@ int project_chunk(const Shape& s, const Chunk& ch, const uint16_t* x, const uint
   g.bseg.row0[2] = (int64_t)(s.Hq + s.Hkv + ch.g0) * d;
   g.C = staging;
   g.ldc = width;
-  g.M = (int)s.L;
+  g.M = (int)s.Lp;
+  g.rows_valid = (int)s.L;
   g.N = ch.kv_first ? width : s.hc * d;
   g.K = s.D;
   g.k_per_split = s.D;
+  g.hm_q = q_rm;
+  g.hm_k = k_rm;
+  g.hm_split = s.hc * d;
+  g.hm_end = ch.kv_first ? (s.hc + s.kc) * d : s.hc * d;
+  g.hm_stride = s.Lp * d;
   // q and k leave the GEMM already rotated: one bf16 rounding after RoPE;
   // v leaves it as fp16 (the forward's P V product takes fp16 operands)
   g.rope_cols = (s.hc + s.kc) * d;
@@ -455,12 +466,11 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     PrepArgs pa;
     memset(&pa, 0, sizeof(pa));
     if (s.proj) {
-      rc = project_chunk(s, ch, x, w_qkv, staging, rope, sb);
+      rc = project_chunk(s, ch, x, w_qkv, staging, q_rm, k_rm, rope, sb);
       if (rc != UPIPE_OK) return rc;
-      pa.src_q = staging;
-      pa.src_k = staging + s.hc * d;
       pa.src_v = staging + (s.hc + s.kc) * d;
       pa.src_ld = width;
+      pa.v_only = 1;  // q and k are in place
     } else {
       pa.src_q = x + (int64_t)ch.h0 * d;
       pa.src_k = x + (int64_t)(s.Hq + ch.g0) * d;
@@ -478,7 +488,8 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pa.v_src_f16 = s.proj ? 1 : 0;
     pa.v_out_f16 = 1;
     pa.v_tiles = 1;
-    UPIPE_TRY(timed(UPIPE_KERNEL_PREP, sb, [&]() { return launch_prep_qkv(pa, rope, sb); }));
+    if (!pa.v_only || pa.nkv > 0)
+      UPIPE_TRY(timed(UPIPE_KERNEL_PREP, sb, [&]() { return launch_prep_qkv(pa, rope, sb); }));
     if (side) {
       UPIPE_TRY(hipEventRecord(side->ready[qslot], sb));
       UPIPE_TRY(hipStreamWaitEvent(st, side->ready[qslot], 0));
@@ -576,12 +587,11 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     PrepArgs pa;
     memset(&pa, 0, sizeof(pa));
     if (s.proj) {
-      rc = project_chunk(s, ch, x, w_qkv, staging, rope, st);
+      rc = project_chunk(s, ch, x, w_qkv, staging, q_rm, k_rm, rope, st);
       if (rc != UPIPE_OK) return rc;
-      pa.src_q = staging;
-      pa.src_k = staging + s.hc * d;
       pa.src_v = staging + (s.hc + s.kc) * d;
       pa.src_ld = width;
+      pa.v_only = 1;  // q and k are in place
     } else {
       pa.src_q = x + (int64_t)ch.h0 * d;
       pa.src_k = x + (int64_t)(s.Hq + ch.g0) * d;
@@ -598,7 +608,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pa.rotate = s.proj ? 0 : 1;
     pa.v_src_f16 = s.proj ? 1 : 0;
     pa.v_out_f16 = 0;
-    UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_qkv(pa, rope, st));
+    if (!pa.v_only || pa.nkv > 0) UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_qkv(pa, rope, st));
 
     // 1b. full recompute: the forward's attention of the chunk's heads again,
     // from the same q, k and (fp16 tile) v, into o_c; it equals the

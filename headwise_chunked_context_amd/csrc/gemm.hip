@@ -167,7 +167,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     if (A_K) {  // ROWS_PER_KB rows of 2 BK bytes per block
       const int row = ROWS_PER_KB * n + lane / CHUNKS;
       const int c = (lane % CHUNKS) ^ kmaj_swz(row);
-      const int m = min(m0 + row, p.M - 1);
+      const int m = min(m0 + row, (p.rows_valid > 0 ? p.rows_valid : p.M) - 1);
       asrc[i] = p.A + (int64_t)m * p.lda + kbeg + c * 8;
       arow[i] = 0;
     } else {    // 4 k rows x 256 bytes of one 128-column half per block
@@ -402,11 +402,17 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
       const int r = c >> 5, cc = c & 31;
       const int m = m0 + half * 128 + r;
       const int n = n0 + cc * 8;
-      if (m < p.M && n < p.N) {
+      const bool head_major = EPI == EPI_STORE_BF16 && n < p.hm_end;
+      const int rows = head_major || p.rows_valid <= 0 ? p.M : p.rows_valid;
+      if (m < rows && n < p.N) {
         const float* src = Cs + r * BN + cc * 8;
         f32x4 lo = *reinterpret_cast<const f32x4*>(src);
         f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
-        u32x4* dst = reinterpret_cast<u32x4*>(C + (int64_t)m * p.ldc + n);
+        u32x4* dst = reinterpret_cast<u32x4*>(
+            !head_major ? C + (int64_t)m * p.ldc + n
+            : n < p.hm_split ? p.hm_q + (int64_t)(n >> 7) * p.hm_stride + (int64_t)m * 128 + (n & 127)
+                             : p.hm_k + (int64_t)((n - p.hm_split) >> 7) * p.hm_stride + (int64_t)m * 128 +
+                                   ((n - p.hm_split) & 127));
         if (EPI == EPI_STORE_BF16 && n < p.rope_cols) {
           // RoPE in fp32 on the four pairs of this 8-column chunk, position m
           float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};

@@ -42,6 +42,19 @@ struct GemmArgs {
   // bf16 store epilogue only: if > 0, output columns n >= f16_from are stored
   // as fp16 (saturated to +-65504) instead of bf16
   int f16_from;
+  // bf16 store epilogue only: columns n < hm_end go to the attention
+  // kernels' head-major buffers [head][Lp][128] instead of C: n < hm_split
+  // to hm_q (head n / 128), the rest to hm_k (head (n - hm_split) / 128);
+  // row m at m * 128 of its head, heads hm_stride elements apart; every row
+  // m < M is stored there
+  uint16_t* hm_q;
+  uint16_t* hm_k;
+  int hm_split, hm_end;
+  int64_t hm_stride;
+  // NT only, if > 0: rows of A that exist (reads of later rows clamp to the
+  // last one) and rows of C that are stored; M may then exceed it, for the
+  // head-major columns' padding rows
+  int rows_valid;
   RopeTable rope;
 };
 
