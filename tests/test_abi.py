@@ -260,3 +260,16 @@ def test_profile_mask_bounds():
     assert L.upipe_profile_read(1, ctypes.byref(ms), ctypes.byref(n)) == B.UPIPE_OK
     assert (ms.value, n.value) == (0.0, 0)
     assert L.upipe_profile_enable(0) == B.UPIPE_OK
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU's share only: --gpus N > 1 exits non-zero
+    with a message (before touching a GPU)."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode != 0
+    assert "one GPU" in (res.stdout + res.stderr)
