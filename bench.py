@@ -312,6 +312,8 @@ def main() -> int:
         "model_flops_per_step": flops,
         "roofline": roofline,
         "kernel_breakdown": breakdown,
+        "kernel_breakdown_from": ("the last warm-up step, every kernel class timed" if prof_steps == 1
+                                  else "the timed steps, every kernel class timed"),
         "workspace_gib": {"fwd": round(ws_f / 2**30, 4), "bwd": round(ws_b / 2**30, 4),
                           "bwd_vs_chunk": ws_vs_chunk},
         "peak_allocated_gib": round(mem0 / 2**30, 3),
