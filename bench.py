@@ -27,6 +27,15 @@ hash matches the current source, else null.
 
 cpu_baseline: the fp64 oracle timed on this host on a bounded sample (the same
 layer shape at a short sequence), reported in the same unit.
+
+workloads: every other layer shape the metric is quoted on, each timed the
+same way for a few steps on inputs drawn on the device (same distributions as
+the seeded host recipe): the small GQA layer, the two one-GPU shares of the
+Llama-3-8B model (q/k/v given, L 524288 and 1048576) and the 32B-class share
+at every head chunk of its sweep.  Each entry gives ms per step, TFLOP/s, the
+dominant kernel's fraction of the bf16 peak, the planner's workspace and the
+allocator's peak, and the HBM rate of the RoPE / layout pass, the dO
+preparation and the dx accumulate (an epilogue of the dx GEMMs).
 """
 from __future__ import annotations
 
@@ -69,6 +78,21 @@ def gemm_flops_per_step(w) -> float:
         return 0.0
     d = w.head_dim
     return 6.0 * w.L * w.hidden * (w.n_q + 2 * w.n_kv) * d + 6.0 * w.L * w.n_q * d * w.hidden
+
+
+def gemm_accum_flops_per_step(w) -> float:
+    """FLOPs of the dx GEMMs after the first chunk (the accumulating ones):
+    2 L hidden K each, K = the chunk's dq columns, plus its dk and dv
+    columns when the chunk completes its KV groups."""
+    if not w.projection:
+        return 0.0
+    d, hc, G = w.head_dim, w.head_chunk, w.n_q // w.n_kv
+    kc = hc // G if hc >= G else 1
+    total = 0.0
+    for c in range(1, w.n_q // hc):
+        kv_last = ((c + 1) * hc) % G == 0
+        total += 2.0 * w.L * w.hidden * ((hc + 2 * kc) * d if kv_last else hc * d)
+    return total
 
 
 def source_hash(rel: str) -> str:
@@ -133,6 +157,172 @@ def copy_calibration() -> None:
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
+def hbm_bytes_per_step(w) -> dict:
+    """Algorithmic HBM bytes per step of the passes that move data rather than
+    contract it, for the classes the library times separately:
+      prep        the RoPE / layout pass, 2 B read + 2 B written per element of
+                  every head it prepares, in the forward and again in the
+                  backward (q/k/v given: every q, k and v head; projection
+                  mode: only v, the GEMM epilogue rotates q and k)
+      prep_dout   dO and O read, dO written (2 B each per element) and per row
+                  LSE read, base-2 LSE and D written (12 B), for every q head
+      gemm_accum  dx read and written (2 B each per element) by the epilogue of
+                  every dx GEMM after the first chunk's; the accumulate is that
+                  GEMM's epilogue, so its rate is these bytes over the whole
+                  (MFMA-bound) GEMM's time, a lower bound of what the epilogue
+                  sustains"""
+    d, L = w.head_dim, w.L
+    heads = (w.n_q + 2 * w.n_kv) if not w.projection else w.n_kv
+    out = {
+        "prep": 2 * heads * L * d * 4.0,
+        "prep_dout": w.n_q * L * (6.0 * d + 12.0),
+    }
+    if w.projection:
+        out["gemm_accum"] = (w.n_q // w.head_chunk - 1) * L * w.hidden * 4.0
+    return out
+
+
+CLASSES = ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm", "gemm_accum")
+
+
+def algo_flops_per_launch(w, kind):
+    """Algorithmic FLOPs per launch (one launch = one head chunk of hc query
+    heads, P = L(L+1)/2 causal pairs):
+      attn_fwd       4 d P hc   (S = Q K^T and O = P V)
+      attn_bwd_dkdv  8 d P hc   (S, dP = dO V^T, dV = P^T dO, dK = dS^T Q)
+      attn_bwd_dq    2 d P hc   (dQ = dS K; its recomputed S and dP, 4 d P hc
+                                 more, are executed, not counted)"""
+    d, hc = w.head_dim, w.head_chunk
+    P = w.L * (w.L + 1) / 2
+    return {"attn_fwd": 4.0 * d * P * hc, "attn_bwd_dkdv": 8.0 * d * P * hc,
+            "attn_bwd_dq": 2.0 * d * P * hc}[kind]
+
+
+def device_inputs(w, seed):
+    """N(0, sigma^2) draws on the device, rounded to bf16: the host recipe's
+    distributions without generating gigabytes on the host."""
+    import torch
+
+    g = torch.Generator(device="cuda:0").manual_seed(seed)
+
+    def draw(shape, sigma):
+        t = torch.randn(*shape, generator=g, device="cuda:0", dtype=torch.float32)
+        if sigma != 1.0:
+            t.mul_(sigma)
+        return t.to(torch.bfloat16)
+
+    d = w.head_dim
+    if w.projection:
+        return (draw((w.L, w.hidden), w.x_sigma), draw((w.qkv_width, w.hidden), w.w_sigma),
+                draw((w.hidden, w.n_q * d), w.w_sigma), draw((w.L, w.hidden), 1.0))
+    return draw((w.L, w.qkv_width), w.x_sigma), None, None, draw((w.L, w.n_q * d), 1.0)
+
+
+def time_layer(lib, w, x, wq, wo, dy, steps, warmup, recompute=False):
+    """Warm-up steps (the last one times every kernel class), then `steps`
+    timed steps with only the dominant class bracketed.  Returns the
+    measurements of one workload."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    hc = w.head_chunk
+    ws_f = lib.workspace_bytes(w.L, w.hidden, w.n_q, w.n_kv, w.head_dim, hc, lib.fwd_pass())
+    bwd_pass = lib.PASS_BWD_RECOMPUTE if recompute else lib.PASS_BWD
+    ws_b = lib.workspace_bytes(w.L, w.hidden, w.n_q, w.n_kv, w.head_dim, hc, bwd_pass)
+    # one workspace, sized for the larger pass, reused by every call
+    ws = torch.empty(max(ws_f, ws_b), dtype=torch.uint8, device=dev)
+
+    def step():
+        _, o, lse = lib.attn_fwd(x, wq, wo, w.n_q, w.n_kv, hc, w.theta, workspace=ws)
+        lib.attn_bwd(x, wq, wo, None if recompute else o, lse, dy, w.n_q, w.n_kv, hc, w.theta,
+                     workspace=ws)
+
+    prof_all = None
+    for i in range(warmup):
+        if i == warmup - 1:
+            torch.cuda.synchronize()
+            lib.profile_enable(True)
+        step()
+    torch.cuda.synchronize()
+    if warmup > 0:
+        prof_all = lib.profile_read()
+        lib.profile_enable(False)
+    dom = None
+    if prof_all is not None:
+        dom = max((k for k in CLASSES if prof_all[k][1] > 0), key=lambda k: prof_all[k][0])
+    lib.profile_enable(True, kinds=None if dom is None else [dom])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = lib.profile_read()
+    lib.profile_enable(False)
+    prof_steps = 1
+    if prof_all is None:
+        prof_all, prof_steps = prof, steps
+        dom = max((k for k in CLASSES if prof[k][1] > 0), key=lambda k: prof[k][0])
+    ms = (t1 - t0) * 1e3 / steps
+    tot_ms, launches = prof[dom]
+    avg_ms = tot_ms / launches
+    if dom == "gemm_accum":
+        per_launch = gemm_accum_flops_per_step(w) * steps / launches
+    elif dom == "gemm":
+        per_launch = (gemm_flops_per_step(w) - gemm_accum_flops_per_step(w)) * steps / launches
+    else:
+        per_launch = algo_flops_per_launch(w, dom)
+    achieved = per_launch / (avg_ms * 1e-3) / 1e12
+    hbm = {}
+    for k, nbytes in hbm_bytes_per_step(w).items():
+        t = prof_all[k][0] / prof_steps
+        if prof_all[k][1] and t > 0:
+            hbm[k] = {"gbs": round(nbytes / (t * 1e-3) / 1e9, 1), "ms_per_step": round(t, 3),
+                      "bytes_per_step": nbytes}
+    return dict(ms=ms, dom=dom, achieved=achieved, avg_ms=avg_ms, launches=launches,
+                prof_all=prof_all, prof_steps=prof_steps, ws_f=ws_f, ws_b=ws_b, hbm=hbm,
+                bwd_pass=bwd_pass)
+
+
+def sweep(lib) -> dict:
+    """Every other workload, a few steps each (inputs drawn on the device)."""
+    import torch
+
+    import synthetic
+
+    W = synthetic.WORKLOADS
+    plan = [(W[1], 3, 10), (W[3], 1, 2), (W[5], 1, 1)]
+    plan += [(W[4].with_(head_chunk=c), 1, 2) for c in (1, 2, 4, 8)]
+    out = {}
+    for w, warmup, steps in plan:
+        key = w.name if w.wid != 4 else f"{w.name}_chunk{w.head_chunk}"
+        torch.cuda.empty_cache()
+        x, wq, wo, dy = device_inputs(w, seed=1000 * w.wid)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()   # the layer's own peak, not the draw's
+        r = time_layer(lib, w, x, wq, wo, dy, steps, warmup)
+        peak = torch.cuda.max_memory_allocated()
+        io = sum(t.numel() * t.element_size() for t in (x, wq, wo, dy) if t is not None)
+        del x, wq, wo, dy
+        flops = model_flops(w)
+        out[key] = {
+            "seq_len": w.L, "hidden": w.hidden, "n_q_heads": w.n_q, "n_kv_heads": w.n_kv,
+            "head_chunk": w.head_chunk, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(r["ms"], 3),
+            "tflops": round(flops / (r["ms"] * 1e-3) / 1e12, 2),
+            "roofline_kernel": r["dom"],
+            "roofline_frac": round(r["achieved"] / PEAK_BF16_TFLOPS, 4),
+            "workspace_gib": {"fwd": round(r["ws_f"] / 2**30, 4), "bwd": round(r["ws_b"] / 2**30, 4)},
+            "peak_allocated_gib": round(peak / 2**30, 3),
+            "peak_allocated_minus_inputs_gib": round((peak - io) / 2**30, 3),
+            "hbm_passes": r["hbm"],
+        }
+        print(f"bench: {key}: {out[key]['ms_per_step']} ms/step, {out[key]['tflops']} TFLOP/s",
+              file=sys.stderr, flush=True)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +336,8 @@ def main() -> int:
     ap.add_argument("--pipeline", action="store_true",
                     help="overlap the forward's next-chunk projection on a second stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="time only the main workload, not the other layer shapes")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -183,86 +375,24 @@ def main() -> int:
     x, wq, wo, dy = (to_dev(inp[k]) for k in ("x", "w_qkv", "w_o", "dy"))
     del inp
     hidden = w.hidden
-    ws_f = lib.workspace_bytes(w.L, hidden, w.n_q, w.n_kv, w.head_dim, hc, lib.fwd_pass())
-    bwd_pass = lib.PASS_BWD_RECOMPUTE if args.recompute else lib.PASS_BWD
-    ws_b = lib.workspace_bytes(w.L, hidden, w.n_q, w.n_kv, w.head_dim, hc, bwd_pass)
-    # one workspace, sized for the larger pass, reused by every call
-    ws = torch.empty(max(ws_f, ws_b), dtype=torch.uint8, device=dev)
-
-    def step():
-        _, o, lse = lib.attn_fwd(x, wq, wo, w.n_q, w.n_kv, hc, w.theta, workspace=ws)
-        lib.attn_bwd(x, wq, wo, None if args.recompute else o, lse, dy, w.n_q, w.n_kv, hc, w.theta,
-                     workspace=ws)
-
-    # The last warm-up step times every kernel class (the breakdown, and which
-    # class dominates); the timed steps bracket only the dominant class's
-    # launches with events, since events around every launch cost ~1% of a
-    # step.  With no warm-up the timed steps bracket every class.
-    prof_all = None
-    for i in range(args.warmup):
-        if i == args.warmup - 1:
-            torch.cuda.synchronize()
-            lib.profile_enable(True)
-        step()
-    torch.cuda.synchronize()
-    if args.warmup > 0:
-        prof_all = lib.profile_read()
-        lib.profile_enable(False)
+    r = time_layer(lib, w, x, wq, wo, dy, args.steps, args.warmup, recompute=args.recompute)
     mem0 = torch.cuda.max_memory_allocated(dev)
-
-    classes = ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm")
-    dom = None
-    if prof_all is not None:
-        dom = max((k for k in classes if prof_all[k][1] > 0), key=lambda k: prof_all[k][0])
-    lib.profile_enable(True, kinds=None if dom is None else [dom])
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    prof = lib.profile_read()
-    lib.profile_enable(False)
-    prof_steps = 1
-    if prof_all is None:
-        prof_all, prof_steps = prof, args.steps
-        dom = max((k for k in classes if prof[k][1] > 0), key=lambda k: prof[k][0])
-
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms, dom, prof_all, prof_steps = r["ms"], r["dom"], r["prof_all"], r["prof_steps"]
+    ws_f, ws_b, bwd_pass = r["ws_f"], r["ws_b"], r["bwd_pass"]
     flops = model_flops(w)
     value = flops / (ms * 1e-3) / 1e12
-
-    # dominant kernel class and its roofline.  Algorithmic FLOPs per launch
-    # (one launch = one head chunk of hc query heads, P = L(L+1)/2 pairs):
-    #   attn_fwd       4 d P hc   (S = Q K^T and O = P V)
-    #   attn_bwd_dkdv  8 d P hc   (S, dP = dO V^T, dV = P^T dO, dK = dS^T Q)
-    #   attn_bwd_dq    2 d P hc   (dQ = dS K; its recomputed S and dP,
-    #                              4 d P hc more, are executed, not counted)
-    #   gemm           the projection GEMMs of a step / their launches
     d = w.head_dim
     P = w.L * (w.L + 1) / 2
-    algo = {
-        "attn_fwd": 4.0 * d * P * hc,
-        "attn_bwd_dkdv": 8.0 * d * P * hc,
-        "attn_bwd_dq": 2.0 * d * P * hc,
-    }
-    tot_ms, launches = prof[dom]
-    avg_ms = tot_ms / launches
-    if dom == "gemm":
-        per_launch = gemm_flops_per_step(w) * args.steps / launches
-    else:
-        per_launch = algo[dom]
-    achieved = per_launch / (avg_ms * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
         "kernel": dom,
-        "achieved": round(achieved, 2),
+        "achieved": round(r["achieved"], 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "frac": round(r["achieved"] / PEAK_BF16_TFLOPS, 4),
         "traffic": traffic_for(dom, w.name) if dom in KERNEL_SOURCES else None,
-        "avg_launch_ms": round(avg_ms, 4),
-        "launches": launches,
+        "avg_launch_ms": round(r["avg_ms"], 4),
+        "launches": r["launches"],
     }
     # the whole attention backward (both kernels) against its 10 d P hc, and
     # the forward, from the step that timed every class
@@ -272,7 +402,8 @@ def main() -> int:
         roofline["attn_bwd_tflops"] = round(10.0 * d * P * hc / (bwd_ms * 1e-3) / 1e12, 2)
     nf = prof_all["attn_fwd"][1]
     if nf:
-        roofline["attn_fwd_tflops"] = round(algo["attn_fwd"] / (prof_all["attn_fwd"][0] / nf * 1e-3) / 1e12, 2)
+        roofline["attn_fwd_tflops"] = round(
+            algo_flops_per_launch(w, "attn_fwd") / (prof_all["attn_fwd"][0] / nf * 1e-3) / 1e12, 2)
     breakdown = {k: {"ms_per_step": round(v[0] / prof_steps, 3), "launches_per_step": v[1] // prof_steps}
                  for k, v in prof_all.items()}
 
@@ -292,7 +423,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 (P V product fp16)",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, rounded to bf16)",
         "config": {
             "workload": w.name,
@@ -317,7 +448,11 @@ def main() -> int:
         "workspace_gib": {"fwd": round(ws_f / 2**30, 4), "bwd": round(ws_b / 2**30, 4),
                           "bwd_vs_chunk": ws_vs_chunk},
         "peak_allocated_gib": round(mem0 / 2**30, 3),
+        "hbm_passes": r["hbm"],
     }
+    if not args.no_sweep and not args.seq_len and args.workload == 2 and not args.chunk:
+        del x, wq, wo, dy
+        out["workloads"] = sweep(lib)
     if not args.no_cpu_baseline and not args.seq_len:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

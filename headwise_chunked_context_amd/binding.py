@@ -38,7 +38,7 @@ EXPORTS = (
 )
 
 KERNEL_KINDS = {"attn_fwd": 0, "attn_bwd_dkdv": 1, "attn_bwd_dq": 2, "gemm": 3, "prep": 4,
-                "finalize": 5}
+                "finalize": 5, "gemm_accum": 6, "prep_dout": 7}
 
 
 class UpipeError(RuntimeError):
@@ -114,7 +114,7 @@ def fwd_pass() -> int:
     return PASS_FWD_PIPELINED if _pipeline else PASS_FWD
 
 
-PROFILE_ALL = 0x3F
+PROFILE_ALL = 0xFF
 
 
 def profile_enable(on: bool, kinds=None) -> None:

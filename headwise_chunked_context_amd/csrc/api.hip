@@ -199,7 +199,7 @@ int check_common(const Shape& s, double theta, const void* x, const void* w_qkv,
   } while (0)
 
 // ---- optional per-kernel-class timing (see upipe_profile_enable)
-constexpr int kKinds = 6;
+constexpr int kKinds = 8;
 static_assert(UPIPE_PROFILE_ALL == (1 << kKinds) - 1, "one mask bit per kernel class");
 struct Profiler {
   int mask = 0;  // bit k: launches of kernel class k are bracketed
@@ -414,20 +414,17 @@ int upipe_attn_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t n_q_head
   return UPIPE_OK;
 }
 
-int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
-                   int32_t head_dim, double rope_theta, int32_t head_chunk, const uint16_t* x,
-                   const uint16_t* w_qkv, const uint16_t* w_o, uint16_t* y, uint16_t* o_saved,
-                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  Shape s;
-  int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
-  if (rc != UPIPE_OK) return rc;
-  const int pass = g_pipeline ? UPIPE_PASS_FWD_PIPELINED : UPIPE_PASS_FWD;
-  rc = check_common(s, rope_theta, x, w_qkv, w_o, workspace, workspace_bytes, pass);
-  if (rc != UPIPE_OK) return rc;
-  if (!o_saved || !lse || s.proj != (y != nullptr)) return UPIPE_EINVAL;
-  if (!aligned16(o_saved) || !aligned16(lse) || (y && !aligned16(y))) return UPIPE_EINVAL;
+}  // extern "C"
 
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+namespace {
+
+// The forward after its argument checks.  `pipelined` selects the two-slot
+// schedule (its workspace layout and second stream).
+int attn_fwd_run(const Shape& s, double rope_theta, const uint16_t* x, const uint16_t* w_qkv,
+                 const uint16_t* w_o, uint16_t* y, uint16_t* o_saved, float* lse, void* workspace,
+                 bool pipelined, hipStream_t st) {
+  int rc = UPIPE_OK;
+  const int pass = pipelined ? UPIPE_PASS_FWD_PIPELINED : UPIPE_PASS_FWD;
   const Plan p = make_plan(s, pass);
   const RopeTable rope = make_rope(rope_theta, s.d);
   const int d = s.d;
@@ -446,7 +443,7 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   // projection half.
   Side* side = nullptr;
   hipStream_t sb = st;
-  if (g_pipeline && nchunks > 1) {
+  if (pipelined && nchunks > 1) {
     rc = side_stream(&side);
     if (rc != UPIPE_OK) return rc;
     sb = side->stream;
@@ -536,6 +533,33 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_NT, EPI_STORE_BF16, g, st));
   }
   return UPIPE_OK;
+}
+
+int check_fwd_outputs(const Shape& s, const uint16_t* y, const uint16_t* o_saved, const float* lse) {
+  if (!o_saved || !lse || s.proj != (y != nullptr)) return UPIPE_EINVAL;
+  if (!aligned16(o_saved) || !aligned16(lse) || (y && !aligned16(y))) return UPIPE_EINVAL;
+  return UPIPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
+                   int32_t head_dim, double rope_theta, int32_t head_chunk, const uint16_t* x,
+                   const uint16_t* w_qkv, const uint16_t* w_o, uint16_t* y, uint16_t* o_saved,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
+  if (rc != UPIPE_OK) return rc;
+  const bool pipelined = g_pipeline;
+  const int pass = pipelined ? UPIPE_PASS_FWD_PIPELINED : UPIPE_PASS_FWD;
+  rc = check_common(s, rope_theta, x, w_qkv, w_o, workspace, workspace_bytes, pass);
+  if (rc != UPIPE_OK) return rc;
+  rc = check_fwd_outputs(s, y, o_saved, lse);
+  if (rc != UPIPE_OK) return rc;
+  return attn_fwd_run(s, rope_theta, x, w_qkv, w_o, y, o_saved, lse, workspace, pipelined,
+                      reinterpret_cast<hipStream_t>(stream));
 }
 
 int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
@@ -693,7 +717,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       pd.src_do = dy + (int64_t)ch.h0 * d;
       pd.do_ld = (int64_t)s.Hq * d;
     }
-    UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_dout(pd, st));
+    UPIPE_LAUNCH(UPIPE_KERNEL_PREP_DOUT, launch_prep_dout(pd, st));
 
     // 3. attention backward: dK/dV of the chunk's KV groups, dQ of its heads
     BwdArgs ba;
@@ -759,7 +783,10 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       g.N = s.D;
       g.K = ncols;
       g.k_per_split = ncols;
-      UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_NN, c == 0 ? EPI_STORE_BF16 : EPI_ACCUM_BF16, g, st));
+      if (c == 0)
+        UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_NN, EPI_STORE_BF16, g, st));
+      else
+        UPIPE_LAUNCH(UPIPE_KERNEL_GEMM_ACCUM, launch_gemm(GEMM_NN, EPI_ACCUM_BF16, g, st));
 
       const int splits = dw_splits(s.L, ncols, s.D);
       GemmArgs w;

@@ -167,10 +167,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-// fp16 pack; values beyond the fp16 range saturate to +-65504
+// fp16 pack of the forward's value operand: finite values beyond the fp16
+// range saturate to +-65504, NaN and +-Inf pass through unchanged.  The
+// finiteness test is on the exponent bits, hidden from the optimizer by an
+// empty asm: device code is built with -fno-honor-nans, under which the
+// compiler turns a visible bit test into a class test that assumes no NaN
+// (and a NaN would then be clamped to -65504).
+__device__ __forceinline__ float sat_f16_range(float x) {
+  uint32_t b = __builtin_bit_cast(uint32_t, x);
+  asm volatile("" : "+v"(b));
+  const float c = fminf(fmaxf(x, -65504.f), 65504.f);
+  return (b & 0x7f800000u) == 0x7f800000u ? x : c;
+}
 __device__ __forceinline__ uint32_t pack_f16x2_sat(float lo, float hi) {
-  lo = fminf(fmaxf(lo, -65504.f), 65504.f);
-  hi = fminf(fmaxf(hi, -65504.f), 65504.f);
+  lo = sat_f16_range(lo);
+  hi = sat_f16_range(hi);
   f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }

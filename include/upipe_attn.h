@@ -64,6 +64,21 @@
  *    Calls on one device must not run concurrently from several host
  *    threads.
  *  - Outputs are fully overwritten (never accumulated into).
+ *
+ * Precision
+ * ---------
+ *  - The projections and the score product Q K^T take bf16 operands with
+ *    fp32 accumulation; the rotated q and k are held in bf16.
+ *  - The forward's O = P V product takes fp16 operands (P in [0, 256], v
+ *    converted from bf16 to fp16) with fp32 accumulation: fp16's 10-bit
+ *    mantissa keeps O inside its error budget where bf16's 7 bits do not.
+ *    Finite |v| > 65504 therefore saturates to +-65504 in the forward (the
+ *    backward uses the bf16 v as given, so its gradients are those of the
+ *    unsaturated v): such inputs are outside the supported range.  NaN and
+ *    +-Inf in v propagate: a non-finite v_j makes that column of O
+ *    non-finite for every query row from j's 64-key tile on (rows of the
+ *    tile before j included, since masked keys enter the tile's product
+ *    with P = 0).
  */
 #ifndef UPIPE_ATTN_H
 #define UPIPE_ATTN_H
@@ -105,7 +120,14 @@ int upipe_attn_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t n_q_head
                                int32_t pass, size_t* bytes);
 
 /*
- * Forward pass.
+ * Forward pass: for each head chunk in turn, project the chunk's q (k and v
+ * when the chunk opens a KV group), rotate, run causal attention and store
+ * the chunk's per-head output; then y = o_saved W_o^T.  The head-at-a-time
+ * schedule with buffers reused by the next group is the one described in
+ * the Untied Ulysses section of "Untied Ulysses Pushes Llama-3-8B Training
+ * to 5 Million Tokens"; the attention itself is exact causal softmax
+ * attention with RoPE ("Untied Ulysses: Memory-Efficient Context
+ * Parallelism via Headwise Chunking", Builds-on list).
  *  x        [L, hidden] bf16 (projection mode) or packed q|k|v (hidden == 0)
  *  w_qkv    [(Hq+2Hkv)*head_dim, hidden] bf16, NULL iff hidden == 0
  *  w_o      [hidden, Hq*head_dim] bf16, NULL iff hidden == 0
@@ -126,8 +148,11 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Backward pass (chain rule of the forward; q/k/v are recomputed per chunk
- * from x, so only o_saved and lse are kept from the forward).
+ * Backward pass: the chain rule of the forward, run chunk by chunk in the
+ * same head-group order with the same buffer reuse (Untied Ulysses section
+ * of "Untied Ulysses Pushes Llama-3-8B Training to 5 Million Tokens");
+ * q/k/v are recomputed per chunk from x, so only o_saved and lse are kept
+ * from the forward.
  *  x, w_qkv, w_o   as in upipe_attn_fwd
  *  o_saved, lse    the forward's outputs for the same inputs.  In projection
  *           mode o_saved may be NULL ("full recompute"): each chunk's
@@ -137,8 +162,13 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
  *           outlive the forward: activation checkpointing, one step of the
  *           memory progression in "Untied Ulysses Pushes Llama-3-8B Training
  *           to 5 Million Tokens", applied to this layer's own saved output.
- *           Needs the UPIPE_PASS_BWD_RECOMPUTE workspace; the results equal
- *           those of the o_saved call bit for bit.
+ *           Needs the UPIPE_PASS_BWD_RECOMPUTE workspace.  dx equals that
+ *           of the o_saved call bit for bit.  dw_qkv and dw_o do too when
+ *           the weight-gradient GEMMs split their reduction over L in at
+ *           most two parts (short L); with more parts the parts meet by
+ *           fp32 atomic adds in an order that varies from run to run, so
+ *           a few bf16 values may differ by one unit in the last place
+ *           between any two calls, with or without o_saved.
  *  dy       [L, hidden] bf16 upstream gradient of y, or dO [L, Hq*head_dim]
  *  dx       [L, hidden] bf16 out, or dqkv [L, (Hq+2Hkv)*head_dim] (hidden == 0)
  *  dw_qkv   [(Hq+2Hkv)*head_dim, hidden] bf16 out, NULL iff hidden == 0
@@ -167,9 +197,12 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
  *   UPIPE_KERNEL_ATTN_FWD      causal attention forward
  *   UPIPE_KERNEL_ATTN_BWD_DKDV causal attention backward, dK and dV
  *   UPIPE_KERNEL_ATTN_BWD_DQ   causal attention backward, dQ
- *   UPIPE_KERNEL_GEMM          projection / gradient GEMMs
- *   UPIPE_KERNEL_PREP          RoPE / layout / dO preparation passes
+ *   UPIPE_KERNEL_GEMM          projection / gradient GEMMs (except below)
+ *   UPIPE_KERNEL_PREP          RoPE / layout pass of q, k, v
  *   UPIPE_KERNEL_FINALIZE      accumulator conversion, fills
+ *   UPIPE_KERNEL_GEMM_ACCUM    the dx GEMMs of the second and later chunks,
+ *                              whose epilogue accumulates into dx in bf16
+ *   UPIPE_KERNEL_PREP_DOUT     dO preparation (D = dO . O, base-2 LSE)
  * State is process-wide and not thread-safe.  Events are host-side HIP
  * objects; no device memory is allocated.  Returns UPIPE_OK, UPIPE_EINVAL
  * (a mask outside 0 .. UPIPE_PROFILE_ALL, a bad kind or NULL output) or
@@ -181,7 +214,9 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
 #define UPIPE_KERNEL_GEMM 3
 #define UPIPE_KERNEL_PREP 4
 #define UPIPE_KERNEL_FINALIZE 5
-#define UPIPE_PROFILE_ALL 0x3F
+#define UPIPE_KERNEL_GEMM_ACCUM 6
+#define UPIPE_KERNEL_PREP_DOUT 7
+#define UPIPE_PROFILE_ALL 0xFF
 int upipe_profile_enable(int mask);
 int upipe_profile_read(int kind, double* total_ms, int64_t* launches);
 

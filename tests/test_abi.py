@@ -107,18 +107,41 @@ def test_workspace_affine_and_shrinking_in_chunk(shape, pss):
             assert max(slopes) == min(slopes), slopes
 
 
+def _per_q_head_bytes(L, D, pss):
+    """Bytes of the workspace buffers that exist once per query head of a
+    chunk, counted buffer by buffer from what each pass holds per q head
+    (Lp = L rounded up to 256, d = 128):
+      forward:  rotated q [Lp, d] bf16; the projection's q columns of the
+                staging block [L, d] bf16 (projection mode)
+      backward: rotated q and dO [Lp, d] bf16 each; the base-2 LSE and
+                D = dO . O rows [Lp] fp32 each; the dq columns of the
+                staging block [L, d] bf16 and the chunk's dW_qkv rows of the
+                fp32 weight-gradient accumulator [d, D] (projection mode)."""
+    Lp, d = -(-L // 256) * 256, 128
+    if pss == B.PASS_FWD:
+        return 2 * Lp * d + (2 * L * d if D else 0)
+    return 2 * (2 * Lp * d) + 2 * (4 * Lp) + ((2 * L * d + 4 * d * D) if D else 0)
+
+
 def test_query_side_reduction_matches_page_figure():
-    """The 32B-share shape (8 q heads, 1 KV head per GPU) at chunk 1 keeps
-    1/8 of the per-query-head workspace it needs at chunk 8."""
+    """The 32B-share shape (8 q heads, 1 KV head per GPU): the planner's
+    growth from chunk 1 to chunk 8 is exactly seven sets of the per-q-head
+    buffers counted one by one, so chunk 1 keeps 1/8 of the q-side
+    intermediates of chunk 8 (the page's 87.5%), while the resident KV
+    group, which chunking cannot shrink, keeps the whole workspace's cut
+    below that figure."""
     fig = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
     want = fig["attention_intermediate_reduction_32b"]["value"]
     L, D = 262144, 5120
     for pss in (B.PASS_FWD, B.PASS_BWD):
-        s = {c: _ws(L, D, 8, 1, 128, c, pss)[1] for c in (1, 2, 8)}
-        per_head = s[2] - s[1]
-        resident = s[1] - per_head          # the part that does not scale with the chunk
-        q1, q8 = s[1] - resident, s[8] - resident
+        s = {c: _ws(L, D, 8, 1, 128, c, pss)[1] for c in (1, 2, 4, 8)}
+        per_head = _per_q_head_bytes(L, D, pss)
+        for c in (2, 4, 8):
+            assert s[c] - s[1] == (c - 1) * per_head, (pss, c)
+        q1, q8 = 1 * per_head, 8 * per_head
         assert abs((1 - q1 / q8) - want) < 1e-12
+        whole = 1 - s[1] / s[8]
+        assert 0 < whole < want, whole
     lo, hi = fig["chunk_sizes_ablated"]["value"]
     assert _ws(L, D, 32, 1, 128, lo, 0)[1] < _ws(L, D, 32, 1, 128, hi, 0)[1]
 
@@ -249,14 +272,15 @@ def test_binding_refuses_host_tensors_before_any_call():
 
 def test_profile_mask_bounds():
     """upipe_profile_enable takes a class mask in 0 .. UPIPE_PROFILE_ALL and
-    refuses anything else; reading a class outside the six is refused too
+    refuses anything else; reading a class outside the eight is refused too
     (host-side state only, no GPU needed)."""
     L = B.lib()
     assert L.upipe_profile_enable(-1) == B.UPIPE_EINVAL
     assert L.upipe_profile_enable(B.PROFILE_ALL + 1) == B.UPIPE_EINVAL
     assert L.upipe_profile_enable(1 << B.KERNEL_KINDS["attn_bwd_dkdv"]) == B.UPIPE_OK
     ms, n = ctypes.c_double(-1), ctypes.c_int64(-1)
-    assert L.upipe_profile_read(6, ctypes.byref(ms), ctypes.byref(n)) == B.UPIPE_EINVAL
+    assert L.upipe_profile_read(len(B.KERNEL_KINDS), ctypes.byref(ms), ctypes.byref(n)) == B.UPIPE_EINVAL
+    assert L.upipe_profile_read(-1, ctypes.byref(ms), ctypes.byref(n)) == B.UPIPE_EINVAL
     assert L.upipe_profile_read(1, ctypes.byref(ms), ctypes.byref(n)) == B.UPIPE_OK
     assert (ms.value, n.value) == (0.0, 0)
     assert L.upipe_profile_enable(0) == B.UPIPE_OK
@@ -273,3 +297,4 @@ def test_bench_refuses_more_than_one_gpu():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode != 0
     assert "one GPU" in (res.stdout + res.stderr)
+
