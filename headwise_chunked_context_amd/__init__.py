@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     PASS_FWD_PIPELINED,
     UPIPE_ECHUNK,
     UPIPE_EHIP,
+    UPIPE_ESCRATCH,
+    STATIC_SCRATCH_BYTES,
     UPIPE_EINVAL,
     UPIPE_EUNSUPPORTED,
     UPIPE_EWORKSPACE,
@@ -19,6 +21,7 @@ from .binding import (  # noqa: F401
     UpipeError,
     attn_bwd,
     attn_fwd,
+    attn_fwd_static,
     fwd_pass,
     lib,
     pipeline_enable,

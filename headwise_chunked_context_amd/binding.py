@@ -19,6 +19,8 @@ UPIPE_EUNSUPPORTED = -2
 UPIPE_ECHUNK = -3
 UPIPE_EWORKSPACE = -4
 UPIPE_EHIP = -5
+UPIPE_ESCRATCH = -6
+STATIC_SCRATCH_BYTES = 256 << 20
 PASS_FWD = 0
 PASS_BWD = 1
 PASS_BWD_RECOMPUTE = 2
@@ -29,6 +31,7 @@ _pipeline = False
 EXPORTS = (
     "upipe_attn_workspace_bytes",
     "upipe_attn_fwd",
+    "upipe_attn_fwd_static",
     "upipe_attn_bwd",
     "upipe_profile_enable",
     "upipe_profile_read",
@@ -67,6 +70,9 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_fwd.argtypes = [i64, i32, i32, i32, i32, f64, i32,
                                  vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.upipe_attn_fwd.restype = ctypes.c_int
+    L.upipe_attn_fwd_static.argtypes = [i64, i32, i32, i32, i32, f64, i32,
+                                        vp, vp, vp, vp, vp, vp, vp]
+    L.upipe_attn_fwd_static.restype = ctypes.c_int
     L.upipe_attn_bwd.argtypes = [i64, i32, i32, i32, i32, f64, i32,
                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.upipe_attn_bwd.restype = ctypes.c_int
@@ -225,6 +231,36 @@ def attn_fwd(x, w_qkv, w_o, n_q: int, n_kv: int, head_chunk: int, theta: float,
                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     if rc != UPIPE_OK:
         raise UpipeError(rc, "upipe_attn_fwd")
+    return y, o_saved, lse
+
+
+def attn_fwd_static(x, w_qkv, w_o, n_q: int, n_kv: int, head_chunk: int, theta: float,
+                    head_dim: int = 128, out=None, stream=None):
+    """Forward through the allocation-free entry point (the library's static
+    scratch instead of a workspace).  Returns (y or None, o_saved, lse);
+    out=(y, o_saved, lse) reuses caller-allocated outputs, so a call then
+    allocates nothing at all."""
+    import torch
+
+    L = _check_inputs(x, w_qkv, w_o, n_q, n_kv, head_dim)
+    proj = w_qkv is not None
+    hidden = x.shape[1] if proj else 0
+    dev = x.device
+    if out is None:
+        y = torch.empty(L, hidden, dtype=torch.bfloat16, device=dev) if proj else None
+        o_saved = torch.empty(L, n_q * head_dim, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(n_q, L, dtype=torch.float32, device=dev)
+    else:
+        y, o_saved, lse = out
+        if proj:
+            _check(y, "y", (L, hidden), torch.bfloat16, dev)
+        _check(o_saved, "o_saved", (L, n_q * head_dim), torch.bfloat16, dev)
+        _check(lse, "lse", (n_q, L), torch.float32, dev)
+    rc = lib().upipe_attn_fwd_static(L, hidden, n_q, n_kv, head_dim, float(theta), head_chunk,
+                                     _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(y), _ptr(o_saved),
+                                     _ptr(lse), _stream(stream))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_attn_fwd_static")
     return y, o_saved, lse
 
 

@@ -398,6 +398,7 @@ const char* upipe_strerror(int status) {
     case UPIPE_ECHUNK: return "head_chunk must divide n_q_heads and not split a KV group's query heads";
     case UPIPE_EWORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than upipe_attn_workspace_bytes";
     case UPIPE_EHIP: return "HIP runtime error while launching a kernel";
+    case UPIPE_ESCRATCH: return "the shapes need more workspace than the static scratch of upipe_attn_fwd_static holds (256 MiB); use upipe_attn_fwd with a workspace";
     default: return "unknown status";
   }
 }
@@ -541,6 +542,28 @@ int check_fwd_outputs(const Shape& s, const uint16_t* y, const uint16_t* o_saved
   return UPIPE_OK;
 }
 
+// ---- the allocation-free forward's scratch: a static device array that
+// stands in for the workspace.  Its host-side name is not a device address:
+// the address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that pointer is handed to kernels.
+constexpr size_t kScratchBytes = UPIPE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return UPIPE_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return UPIPE_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return UPIPE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -560,6 +583,32 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   if (rc != UPIPE_OK) return rc;
   return attn_fwd_run(s, rope_theta, x, w_qkv, w_o, y, o_saved, lse, workspace, pipelined,
                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int upipe_attn_fwd_static(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
+                          int32_t head_dim, double rope_theta, int32_t head_chunk,
+                          const uint16_t* x, const uint16_t* w_qkv, const uint16_t* w_o,
+                          uint16_t* y, uint16_t* o_saved, float* lse, void* stream) {
+  Shape s;
+  int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
+  if (rc != UPIPE_OK) return rc;
+  if (make_plan(s, UPIPE_PASS_FWD).total > kScratchBytes) return UPIPE_ESCRATCH;
+  // the scratch stands in for the workspace argument of the checks
+  rc = check_common(s, rope_theta, x, w_qkv, w_o, reinterpret_cast<void*>(kAlign), kScratchBytes,
+                    UPIPE_PASS_FWD);
+  if (rc != UPIPE_OK) return rc;
+  rc = check_fwd_outputs(s, y, o_saved, lse);
+  if (rc != UPIPE_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_ptr(&ws);
+  if (rc != UPIPE_OK) return rc;
+  // one stream, no profiling events: nothing is created or allocated
+  const int mask = g_prof.mask;
+  g_prof.mask = 0;
+  rc = attn_fwd_run(s, rope_theta, x, w_qkv, w_o, y, o_saved, lse, ws, false,
+                    reinterpret_cast<hipStream_t>(stream));
+  g_prof.mask = mask;
+  return rc;
 }
 
 int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,

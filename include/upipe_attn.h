@@ -98,6 +98,8 @@ extern "C" {
 #define UPIPE_ECHUNK (-3)       /* head_chunk does not divide Hq or straddles a KV group */
 #define UPIPE_EWORKSPACE (-4)   /* workspace NULL, misaligned or smaller than required */
 #define UPIPE_EHIP (-5)         /* the HIP runtime reported an error at launch    */
+#define UPIPE_ESCRATCH (-6)     /* upipe_attn_fwd_static: the shapes need more
+                                   workspace than its static scratch holds        */
 
 #define UPIPE_PASS_FWD 0
 #define UPIPE_PASS_BWD 1
@@ -146,6 +148,32 @@ int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
                    const uint16_t* x, const uint16_t* w_qkv, const uint16_t* w_o,
                    uint16_t* y, uint16_t* o_saved, float* lse,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same computation, arguments and results as
+ * upipe_attn_fwd with the one-stream schedule, but the workspace is a
+ * static device array of the library, UPIPE_STATIC_SCRATCH_BYTES (256 MiB)
+ * per GPU, held from library load until the process ends (each GPU the
+ * library runs on has its own copy; its address is looked up on the first
+ * call on that device).  The call allocates nothing: no device memory, no
+ * stream or event (pipelining and profiling are not applied to it).
+ * Returns UPIPE_ESCRATCH, before any GPU work, when upipe_attn_workspace_bytes
+ * for UPIPE_PASS_FWD exceeds the scratch (for example L = 32768, hidden 4096,
+ * 32 q / 8 KV heads fits up to head_chunk 8); otherwise as upipe_attn_fwd.
+ * Every call on one GPU uses the same scratch and leaves its contents
+ * behind: calls on one GPU that may overlap in time (different streams,
+ * host threads or processes sharing the library instance) race on it and
+ * must be serialized by the caller.  Nothing in the scratch needs to start
+ * at any value.
+ */
+#define UPIPE_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+int upipe_attn_fwd_static(int64_t seq_len, int32_t hidden, int32_t n_q_heads,
+                          int32_t n_kv_heads, int32_t head_dim, double rope_theta,
+                          int32_t head_chunk, const uint16_t* x, const uint16_t* w_qkv,
+                          const uint16_t* w_o, uint16_t* y, uint16_t* o_saved, float* lse,
+                          void* stream);
 
 /*
  * Backward pass: the chain rule of the forward, run chunk by chunk in the

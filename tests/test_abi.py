@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 def test_strerror_covers_every_status():
     seen = set()
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         msg = hc_amd.strerror(code)
         assert msg and msg not in seen
         seen.add(msg)
@@ -298,3 +298,35 @@ def test_bench_refuses_more_than_one_gpu():
     assert res.returncode != 0
     assert "one GPU" in (res.stdout + res.stderr)
 
+
+def _fwd_static(**kw):
+    a = dict(L=1024, D=1024, nq=8, nkv=2, d=128, theta=5e5, hc=2,
+             x=P, wqkv=P, wo=P, y=P, o=P, lse=P)
+    a.update(kw)
+    return hc_amd.lib().upipe_attn_fwd_static(a["L"], a["D"], a["nq"], a["nkv"], a["d"],
+                                              a["theta"], a["hc"], a["x"], a["wqkv"], a["wo"],
+                                              a["y"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=32768, D=4096, nq=32, nkv=8, hc=16), B.UPIPE_ESCRATCH),   # 384 MiB > 256 MiB
+    (dict(L=524288, D=0, nq=4, nkv=1, hc=1, wqkv=None, wo=None, y=None), B.UPIPE_ESCRATCH),
+    (dict(hc=3), B.UPIPE_ECHUNK),
+    (dict(o=None), B.UPIPE_EINVAL),
+    (dict(lse=None), B.UPIPE_EINVAL),
+    (dict(y=None), B.UPIPE_EINVAL),                     # projection mode needs y
+    (dict(wo=None), B.UPIPE_EINVAL),
+    (dict(theta=-1.0), B.UPIPE_EINVAL),
+    (dict(x=P + 8), B.UPIPE_EINVAL),                    # misaligned
+])
+def test_static_forward_checks_before_any_gpu_work(kw, code):
+    """The allocation-free forward refuses bad arguments, and shapes whose
+    workspace exceeds its static scratch, on the host (no GPU here)."""
+    assert _fwd_static(**kw) == code
+
+
+def test_static_scratch_limit_covers_the_benchmarked_forward():
+    """L 32768, hidden 4096, 32 q / 8 KV heads: chunk 8 fits the scratch,
+    chunk 16 does not."""
+    assert _ws(32768, 4096, 32, 8, 128, 8, B.PASS_FWD)[1] <= B.STATIC_SCRATCH_BYTES
+    assert _ws(32768, 4096, 32, 8, 128, 16, B.PASS_FWD)[1] > B.STATIC_SCRATCH_BYTES
