@@ -227,7 +227,7 @@ def time_layer(lib, w, x, wq, wo, dy, steps, warmup, recompute=False):
     dev = torch.device("cuda:0")
     hc = w.head_chunk
     ws_f = lib.workspace_bytes(w.L, w.hidden, w.n_q, w.n_kv, w.head_dim, hc, lib.fwd_pass())
-    bwd_pass = lib.PASS_BWD_RECOMPUTE if recompute else lib.PASS_BWD
+    bwd_pass = lib.bwd_pass(recompute)
     ws_b = lib.workspace_bytes(w.L, w.hidden, w.n_q, w.n_kv, w.head_dim, hc, bwd_pass)
     # one workspace, sized for the larger pass, reused by every call
     ws = torch.empty(max(ws_f, ws_b), dtype=torch.uint8, device=dev)
@@ -291,24 +291,32 @@ def sweep(lib) -> dict:
     import synthetic
 
     W = synthetic.WORKLOADS
-    plan = [(W[1], 3, 10), (W[3], 1, 2), (W[5], 1, 1)]
-    plan += [(W[4].with_(head_chunk=c), 1, 2) for c in (1, 2, 4, 8)]
+    plan = [(W[1], 3, 10, False), (W[3], 1, 2, False), (W[5], 1, 1, False)]
+    # the 32B-class share at every chunk of its sweep, on one stream and with
+    # the two-slot pipeline (next chunk's preparation on a second stream)
+    plan += [(W[4].with_(head_chunk=c), 1, 2, pipe) for pipe in (False, True) for c in (1, 2, 4, 8)]
     out = {}
-    for w, warmup, steps in plan:
+    for w, warmup, steps, pipe in plan:
         key = w.name if w.wid != 4 else f"{w.name}_chunk{w.head_chunk}"
+        if pipe:
+            key += "_pipelined"
         torch.cuda.empty_cache()
         x, wq, wo, dy = device_inputs(w, seed=1000 * w.wid)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()   # the layer's own peak, not the draw's
-        r = time_layer(lib, w, x, wq, wo, dy, steps, warmup)
+        lib.pipeline_enable(pipe)
+        try:
+            r = time_layer(lib, w, x, wq, wo, dy, steps, warmup)
+        finally:
+            lib.pipeline_enable(False)
         peak = torch.cuda.max_memory_allocated()
         io = sum(t.numel() * t.element_size() for t in (x, wq, wo, dy) if t is not None)
         del x, wq, wo, dy
         flops = model_flops(w)
         out[key] = {
             "seq_len": w.L, "hidden": w.hidden, "n_q_heads": w.n_q, "n_kv_heads": w.n_kv,
-            "head_chunk": w.head_chunk, "steps": steps, "warmup": warmup,
+            "head_chunk": w.head_chunk, "pipeline": pipe, "steps": steps, "warmup": warmup,
             "ms_per_step": round(r["ms"], 3),
             "tflops": round(flops / (r["ms"] * 1e-3) / 1e12, 2),
             "roofline_kernel": r["dom"],

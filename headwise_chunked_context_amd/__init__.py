@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     PASS_BWD_RECOMPUTE,
     PASS_FWD,
     PASS_FWD_PIPELINED,
+    PASS_BWD_PIPELINED,
     UPIPE_ECHUNK,
     UPIPE_EHIP,
     UPIPE_ESCRATCH,
@@ -23,6 +24,7 @@ from .binding import (  # noqa: F401
     attn_fwd,
     attn_fwd_static,
     fwd_pass,
+    bwd_pass,
     lib,
     pipeline_enable,
     profile_enable,

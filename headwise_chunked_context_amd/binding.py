@@ -25,6 +25,7 @@ PASS_FWD = 0
 PASS_BWD = 1
 PASS_BWD_RECOMPUTE = 2
 PASS_FWD_PIPELINED = 3
+PASS_BWD_PIPELINED = 4
 _pipeline = False
 
 # names declared in include/upipe_attn.h
@@ -106,8 +107,9 @@ def workspace_bytes(L: int, hidden: int, n_q: int, n_kv: int, head_dim: int, hea
 
 
 def pipeline_enable(on: bool) -> None:
-    """Two-slot pipelining of the forward on a second stream (default off;
-    needs the PASS_FWD_PIPELINED workspace while on)."""
+    """Two-slot pipelining of the forward and the saved-output backward on a
+    second stream (default off; needs the PASS_*_PIPELINED workspaces while
+    on)."""
     global _pipeline
     rc = lib().upipe_pipeline_enable(1 if on else 0)
     if rc != UPIPE_OK:
@@ -118,6 +120,14 @@ def pipeline_enable(on: bool) -> None:
 def fwd_pass() -> int:
     """Workspace pass of upipe_attn_fwd under the current pipelining setting."""
     return PASS_FWD_PIPELINED if _pipeline else PASS_FWD
+
+
+def bwd_pass(recompute: bool = False) -> int:
+    """Workspace pass of upipe_attn_bwd under the current pipelining setting
+    (the full-recompute backward is never pipelined)."""
+    if recompute:
+        return PASS_BWD_RECOMPUTE
+    return PASS_BWD_PIPELINED if _pipeline else PASS_BWD
 
 
 PROFILE_ALL = 0xFF
@@ -282,7 +292,7 @@ def attn_bwd(x, w_qkv, w_o, o_saved, lse, dy, n_q: int, n_kv: int, head_chunk: i
     dx = torch.empty_like(x)
     dw_qkv = torch.empty_like(w_qkv) if proj else None
     dw_o = torch.empty_like(w_o) if proj else None
-    pass_ = PASS_BWD if o_saved is not None else PASS_BWD_RECOMPUTE
+    pass_ = bwd_pass(recompute=o_saved is None)
     ws_n = workspace_bytes(L, hidden, n_q, n_kv, head_dim, head_chunk, pass_)
     ws = _workspace(ws_n, dev, workspace)
     rc = lib().upipe_attn_bwd(L, hidden, n_q, n_kv, head_dim, float(theta), head_chunk,

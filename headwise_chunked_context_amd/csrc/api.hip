@@ -106,7 +106,8 @@ struct Plan {
   size_t staging;              // [L][(hc+2kc)d] bf16 GEMM output / gradient staging
   size_t q_rm;                 // [hc][Lp][d] bf16, rotated
   size_t k_rm, v_rm;           // [kc][Lp][d] bf16 (k rotated; v fp16 in the forward)
-  size_t q_rm2, k_rm2, v_rm2;  // the same, second slot (forward pipeline)
+  size_t q_rm2, k_rm2, v_rm2;  // the same, second slot (forward and backward pipeline)
+  size_t staging2, do_rm2, lse2_2, dvec2, dw_acc2;  // second slot (backward pipeline)
   size_t do_rm;                // [hc][Lp][d] bf16 (bwd)
   size_t lse2, dvec;           // [hc][Lp] fp32 (bwd)
   size_t dk_acc, dv_acc;       // [kc][Lp][d] fp32 (bwd, only when a group spans chunks)
@@ -133,7 +134,7 @@ Plan make_plan(const Shape& s, int pass) {
   p.q_rm = take(hc * head_bf16);
   p.k_rm = take(kc * head_bf16);
   p.v_rm = take(kc * head_bf16);
-  if (pass == UPIPE_PASS_FWD_PIPELINED) {
+  if (pass == UPIPE_PASS_FWD_PIPELINED || pass == UPIPE_PASS_BWD_PIPELINED) {
     // the next chunk's q/k/v are prepared while this chunk's attention runs
     p.q_rm2 = take(hc * head_bf16);
     p.k_rm2 = take(kc * head_bf16);
@@ -142,7 +143,17 @@ Plan make_plan(const Shape& s, int pass) {
     p.q_rm2 = p.k_rm2 = p.v_rm2 = no;
   }
   p.o_c = p.v_t = no;
-  if (pass == UPIPE_PASS_BWD || pass == UPIPE_PASS_BWD_RECOMPUTE) {
+  p.staging2 = p.do_rm2 = p.lse2_2 = p.dvec2 = p.dw_acc2 = no;
+  if (pass == UPIPE_PASS_BWD_PIPELINED) {
+    // the rest of the next chunk's slot: its staging block, dO, LSE2 and D
+    // rows and its weight-gradient accumulator
+    p.staging2 = s.proj ? take((size_t)s.L * width * 2) : no;
+    p.do_rm2 = take(hc * head_bf16);
+    p.lse2_2 = take(hc * Lp * 4);
+    p.dvec2 = take(hc * Lp * 4);
+    p.dw_acc2 = s.proj ? take(width * (size_t)s.D * 4) : no;
+  }
+  if (pass == UPIPE_PASS_BWD || pass == UPIPE_PASS_BWD_RECOMPUTE || pass == UPIPE_PASS_BWD_PIPELINED) {
     p.do_rm = take(hc * head_bf16);
     p.lse2 = take(hc * Lp * 4);
     p.dvec = take(hc * Lp * 4);
@@ -406,7 +417,7 @@ const char* upipe_strerror(int status) {
 int upipe_attn_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t n_q_heads,
                                int32_t n_kv_heads, int32_t head_dim, int32_t head_chunk,
                                int32_t pass, size_t* bytes) {
-  if (!bytes || pass < UPIPE_PASS_FWD || pass > UPIPE_PASS_FWD_PIPELINED) return UPIPE_EINVAL;
+  if (!bytes || pass < UPIPE_PASS_FWD || pass > UPIPE_PASS_BWD_PIPELINED) return UPIPE_EINVAL;
   Shape s;
   int rc = check_shape(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, head_chunk, &s);
   if (rc != UPIPE_OK) return rc;
@@ -622,7 +633,10 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   // o_saved == NULL: recompute each chunk's attention output (projection mode)
   const bool recompute = o_saved == nullptr;
   if (recompute && !s.proj) return UPIPE_EINVAL;
-  const int pass = recompute ? UPIPE_PASS_BWD_RECOMPUTE : UPIPE_PASS_BWD;
+  // the two-slot schedule applies to the saved-output backward
+  const bool pipelined = g_pipeline && !recompute;
+  const int pass = recompute ? UPIPE_PASS_BWD_RECOMPUTE
+                             : (pipelined ? UPIPE_PASS_BWD_PIPELINED : UPIPE_PASS_BWD);
   rc = check_common(s, rope_theta, x, w_qkv, w_o, workspace, workspace_bytes, pass);
   if (rc != UPIPE_OK) return rc;
   if (!lse || !dy || !dx) return UPIPE_EINVAL;
@@ -637,32 +651,43 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   const int d = s.d;
   const int64_t qkv_ld = (int64_t)(s.Hq + 2 * s.Hkv) * d;
   const int width = (s.hc + 2 * s.kc) * d;
-  uint16_t* staging = at<uint16_t>(workspace, p.staging);
-  uint16_t* q_rm = at<uint16_t>(workspace, p.q_rm);
-  uint16_t* k_rm = at<uint16_t>(workspace, p.k_rm);
-  uint16_t* v_rm = at<uint16_t>(workspace, p.v_rm);
-  uint16_t* do_rm = at<uint16_t>(workspace, p.do_rm);
-  float* lse2 = at<float>(workspace, p.lse2);
-  float* dvec = at<float>(workspace, p.dvec);
+  const int nchunks = s.Hq / s.hc;
+  // per-chunk buffers, two slots in the pipelined schedule (the second slot
+  // of a single-slot plan is the first)
+  auto slot2 = [&](size_t a, size_t b) { return b == (size_t)-1 ? a : b; };
+  uint16_t* staging[2] = {at<uint16_t>(workspace, p.staging), at<uint16_t>(workspace, slot2(p.staging, p.staging2))};
+  uint16_t* q_rm[2] = {at<uint16_t>(workspace, p.q_rm), at<uint16_t>(workspace, slot2(p.q_rm, p.q_rm2))};
+  uint16_t* k_rm[2] = {at<uint16_t>(workspace, p.k_rm), at<uint16_t>(workspace, slot2(p.k_rm, p.k_rm2))};
+  uint16_t* v_rm[2] = {at<uint16_t>(workspace, p.v_rm), at<uint16_t>(workspace, slot2(p.v_rm, p.v_rm2))};
+  uint16_t* do_rm[2] = {at<uint16_t>(workspace, p.do_rm), at<uint16_t>(workspace, slot2(p.do_rm, p.do_rm2))};
+  float* lse2[2] = {at<float>(workspace, p.lse2), at<float>(workspace, slot2(p.lse2, p.lse2_2))};
+  float* dvec[2] = {at<float>(workspace, p.dvec), at<float>(workspace, slot2(p.dvec, p.dvec2))};
+  float* dw_acc[2] = {at<float>(workspace, p.dw_acc), at<float>(workspace, slot2(p.dw_acc, p.dw_acc2))};
   float* dk_acc = at<float>(workspace, p.dk_acc);
   float* dv_acc = at<float>(workspace, p.dv_acc);
-  float* dw_acc = at<float>(workspace, p.dw_acc);
   uint16_t* o_c = at<uint16_t>(workspace, p.o_c);
   uint16_t* v_t = at<uint16_t>(workspace, p.v_t);
+  const size_t dw_bytes = (size_t)width * s.D * 4;
 
-  // the weight-gradient accumulator starts at zero; each conversion pass
+  // the weight-gradient accumulators start at zero; each conversion pass
   // clears what it consumed
-  if (dw_acc) UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_zero(dw_acc, (size_t)width * s.D * 4, st));
+  if (dw_acc[0]) {
+    UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_zero(dw_acc[0], dw_bytes, st));
+    if (dw_acc[1] != dw_acc[0]) UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_zero(dw_acc[1], dw_bytes, st));
+  }
 
-  for (int c = 0; c < s.Hq / s.hc; ++c) {
+  // ---- stage 1 of chunk c on stream `sq` (buffers of slot `sl`, KV slot
+  // `kl`): recompute the rotated q (k, v at a group start), the attention
+  // output in recompute mode, dO, D and the base-2 LSE, and dW_o
+  auto stage_prepare = [&](int c, int sl, int kl, hipStream_t sq) -> int {
     const Chunk ch = chunk_info(s, c);
     // 1. recompute the chunk's rotated q (and k, v at a group start)
     PrepArgs pa;
     memset(&pa, 0, sizeof(pa));
     if (s.proj) {
-      rc = project_chunk(s, ch, x, w_qkv, staging, q_rm, k_rm, rope, st);
-      if (rc != UPIPE_OK) return rc;
-      pa.src_v = staging + (s.hc + s.kc) * d;
+      const int r = project_chunk(s, ch, x, w_qkv, staging[sl], q_rm[sl], k_rm[kl], rope, sq);
+      if (r != UPIPE_OK) return r;
+      pa.src_v = staging[sl] + (s.hc + s.kc) * d;
       pa.src_ld = width;
       pa.v_only = 1;  // q and k are in place
     } else {
@@ -673,15 +698,16 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     }
     pa.nq = s.hc;
     pa.nkv = ch.kv_first ? s.kc : 0;
-    pa.q_rm = q_rm;
-    pa.k_rm = k_rm;
-    pa.v_rm = v_rm;
+    pa.q_rm = q_rm[sl];
+    pa.k_rm = k_rm[kl];
+    pa.v_rm = v_rm[kl];
     pa.L = s.L;
     pa.Lp = s.Lp;
     pa.rotate = s.proj ? 0 : 1;
     pa.v_src_f16 = s.proj ? 1 : 0;
     pa.v_out_f16 = 0;
-    if (!pa.v_only || pa.nkv > 0) UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_qkv(pa, rope, st));
+    if (!pa.v_only || pa.nkv > 0)
+      UPIPE_TRY(timed(UPIPE_KERNEL_PREP, sq, [&]() { return launch_prep_qkv(pa, rope, sq); }));
 
     // 1b. full recompute: the forward's attention of the chunk's heads again,
     // from the same q, k and (fp16 tile) v, into o_c; it equals the
@@ -693,12 +719,12 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
         pv.v_rm = v_t;
         pv.v_out_f16 = 1;
         pv.v_tiles = 1;
-        UPIPE_LAUNCH(UPIPE_KERNEL_PREP, launch_prep_qkv(pv, rope, st));
+        UPIPE_TRY(timed(UPIPE_KERNEL_PREP, sq, [&]() { return launch_prep_qkv(pv, rope, sq); }));
       }
       FwdArgs fa;
       memset(&fa, 0, sizeof(fa));
-      fa.q = q_rm;
-      fa.k = k_rm;
+      fa.q = q_rm[sl];
+      fa.k = k_rm[kl];
       fa.v = v_t;
       fa.nh = s.hc;
       fa.group = s.G;
@@ -707,11 +733,11 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       fa.o_head0 = ch.h0;
       fa.o = o_c;
       fa.o_ld = (int64_t)s.hc * d;
-      fa.lse = lse2;
+      fa.lse = lse2[sl];
       fa.L = s.L;
       fa.Lp = s.Lp;
       fa.scale_log2 = kLog2e / sqrtf((float)d);
-      UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_FWD, launch_flash_fwd(fa, st));
+      UPIPE_TRY(timed(UPIPE_KERNEL_ATTN_FWD, sq, [&]() { return launch_flash_fwd(fa, sq); }));
     }
     const uint16_t* o_chunk = recompute ? o_c : o_saved + (int64_t)ch.h0 * d;
     const int64_t o_chunk_ld = recompute ? (int64_t)s.hc * d : (int64_t)s.Hq * d;
@@ -722,9 +748,9 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pd.o_ld = o_chunk_ld;
     pd.lse = lse + (int64_t)ch.h0 * s.L;
     pd.nh = s.hc;
-    pd.do_rm = do_rm;
-    pd.lse2 = lse2;
-    pd.dvec = dvec;
+    pd.do_rm = do_rm[sl];
+    pd.lse2 = lse2[sl];
+    pd.dvec = dvec[sl];
     pd.L = s.L;
     pd.Lp = s.Lp;
     if (s.proj) {
@@ -734,14 +760,14 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       g.lda = s.D;
       g.B = w_o + (int64_t)ch.h0 * d;
       g.ldb = (int64_t)s.Hq * d;
-      g.C = staging;
+      g.C = staging[sl];
       g.ldc = s.hc * d;
       g.M = (int)s.L;
       g.N = s.hc * d;
       g.K = s.D;
       g.k_per_split = s.D;
-      UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_NN, EPI_STORE_BF16, g, st));
-      pd.src_do = staging;
+      UPIPE_TRY(timed(UPIPE_KERNEL_GEMM, sq, [&]() { return launch_gemm(GEMM_NN, EPI_STORE_BF16, g, sq); }));
+      pd.src_do = staging[sl];
       pd.do_ld = s.hc * d;
 
       // dW_o[:, cols] = dy^T O_c   (reduction over the sequence, split-K)
@@ -752,39 +778,47 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       w.lda = s.D;
       w.B = o_chunk;
       w.ldb = o_chunk_ld;
-      w.C = dw_acc;
+      w.C = dw_acc[sl];
       w.M = s.D;
       w.N = s.hc * d;
       w.K = (int)s.L;
       w.k_per_split = k_per_split(s.L, splits);
-      UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, st));
+      UPIPE_TRY(timed(UPIPE_KERNEL_GEMM, sq, [&]() { return launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, sq); }));
       RowSegments ident;
       memset(&ident, 0, sizeof(ident));
-      UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_acc_to_bf16(dw_acc, s.D, s.hc * d, dw_o + (int64_t)ch.h0 * d,
-                                   (int64_t)s.Hq * d, ident, st));
+      UPIPE_TRY(timed(UPIPE_KERNEL_FINALIZE, sq, [&]() {
+        return launch_acc_to_bf16(dw_acc[sl], s.D, s.hc * d, dw_o + (int64_t)ch.h0 * d,
+                                  (int64_t)s.Hq * d, ident, sq);
+      }));
     } else {
       pd.src_do = dy + (int64_t)ch.h0 * d;
       pd.do_ld = (int64_t)s.Hq * d;
     }
-    UPIPE_LAUNCH(UPIPE_KERNEL_PREP_DOUT, launch_prep_dout(pd, st));
+    UPIPE_TRY(timed(UPIPE_KERNEL_PREP_DOUT, sq, [&]() { return launch_prep_dout(pd, sq); }));
+    return UPIPE_OK;
+  };
 
+  // ---- stage 2 of chunk c on the caller's stream: the attention backward
+  // (dK/dV of the chunk's KV groups, dQ of its heads), then dx and dW_qkv
+  auto stage_attend = [&](int c, int sl, int kl) -> int {
+    const Chunk ch = chunk_info(s, c);
     // 3. attention backward: dK/dV of the chunk's KV groups, dQ of its heads
     BwdArgs ba;
-    ba.q = q_rm;
-    ba.k = k_rm;
-    ba.v = v_rm;
-    ba.dO = do_rm;
-    ba.lse2 = lse2;
-    ba.dvec = dvec;
+    ba.q = q_rm[sl];
+    ba.k = k_rm[kl];
+    ba.v = v_rm[kl];
+    ba.dO = do_rm[sl];
+    ba.lse2 = lse2[sl];
+    ba.dvec = dvec[sl];
     ba.dk_acc = dk_acc;
     ba.dv_acc = dv_acc;
     ba.kv_first = ch.kv_first ? 1 : 0;
     ba.kv_last = ch.kv_last ? 1 : 0;
     if (s.proj) {   // rows of [dq | dk | dv] for this chunk, in the staging buffer
-      ba.dq_out = staging;
+      ba.dq_out = staging[sl];
       ba.dq_ld = width;
-      ba.dk_out = staging + s.hc * d;
-      ba.dv_out = staging + (s.hc + s.kc) * d;
+      ba.dk_out = staging[sl] + s.hc * d;
+      ba.dv_out = staging[sl] + (s.hc + s.kc) * d;
       ba.out_ld = width;
     } else {        // straight into the caller's dqkv
       ba.dq_out = dx + (int64_t)ch.h0 * d;
@@ -821,7 +855,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
 
       GemmArgs g;
       memset(&g, 0, sizeof(g));
-      g.A = staging;
+      g.A = staging[sl];
       g.lda = width;
       g.B = w_qkv;
       g.ldb = s.D;
@@ -840,18 +874,74 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       const int splits = dw_splits(s.L, ncols, s.D);
       GemmArgs w;
       memset(&w, 0, sizeof(w));
-      w.A = staging;
+      w.A = staging[sl];
       w.lda = width;
       w.B = x;
       w.ldb = s.D;
-      w.C = dw_acc;
+      w.C = dw_acc[sl];
       w.M = ncols;
       w.N = s.D;
       w.K = (int)s.L;
       w.k_per_split = k_per_split(s.L, splits);
       UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, st));
-      UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_acc_to_bf16(dw_acc, ncols, s.D, dw_qkv, s.D, seg, st));
+      UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_acc_to_bf16(dw_acc[sl], ncols, s.D, dw_qkv, s.D, seg, st));
     }
+    return UPIPE_OK;
+  };
+
+  if (!pipelined || nchunks == 1) {
+    for (int c = 0; c < nchunks; ++c) {
+      rc = stage_prepare(c, 0, 0, st);
+      if (rc != UPIPE_OK) return rc;
+      rc = stage_attend(c, 0, 0);
+      if (rc != UPIPE_OK) return rc;
+    }
+    return UPIPE_OK;
+  }
+
+  // ---- two-slot schedule: chunk c+1's preparation (projection, RoPE and
+  // layout, dO, dW_o) runs on a second stream into the other slot while
+  // chunk c's attention backward and dx/dW_qkv run on the caller's stream.
+  // Chunk c uses slot c % 2; a KV group's k/v use the slot after the
+  // previous group's.  The preparation of chunk c waits for chunk c - 2's
+  // stage 2 (the last reader of every buffer of its slot; a KV slot's last
+  // reader is at least as early), stage 2 of chunk c for its preparation.
+  // Stage 2 runs in chunk order on one stream, which orders the dK/dV
+  // accumulators and the dx accumulate.
+  Side* side = nullptr;
+  rc = side_stream(&side);
+  if (rc != UPIPE_OK) return rc;
+  hipStream_t sb = side->stream;
+  UPIPE_TRY(hipEventRecord(side->fork, st));   // after the accumulator fills
+  UPIPE_TRY(hipStreamWaitEvent(sb, side->fork, 0));
+  int kslot_of[2] = {0, 0};                     // KV slot of the chunk in each slot
+  int kslot = 1;
+  auto prepare = [&](int c) -> int {
+    const Chunk ch = chunk_info(s, c);
+    const int sl = c & 1;
+    if (ch.kv_first) kslot ^= 1;
+    kslot_of[sl] = kslot;
+    if (c >= 2 && hipStreamWaitEvent(sb, side->done[sl], 0) != hipSuccess) return UPIPE_EHIP;
+    const int r = stage_prepare(c, sl, kslot, sb);
+    if (r != UPIPE_OK) return r;
+    if (hipEventRecord(side->ready[sl], sb) != hipSuccess) return UPIPE_EHIP;
+    return UPIPE_OK;
+  };
+  rc = prepare(0);
+  if (rc != UPIPE_OK) return rc;
+  for (int c = 0; c < nchunks; ++c) {
+    const int sl = c & 1;
+    const int kl = kslot_of[sl];
+    if (c + 1 < nchunks) {
+      rc = prepare(c + 1);
+      if (rc != UPIPE_OK) return rc;
+    }
+    // the ready event of this slot was recorded for chunk c before chunk
+    // c+1's preparation re-recorded the other slot's
+    UPIPE_TRY(hipStreamWaitEvent(st, side->ready[sl], 0));
+    rc = stage_attend(c, sl, kl);
+    if (rc != UPIPE_OK) return rc;
+    UPIPE_TRY(hipEventRecord(side->done[sl], st));
   }
   return UPIPE_OK;
 }

@@ -105,12 +105,14 @@ extern "C" {
 #define UPIPE_PASS_BWD 1
 #define UPIPE_PASS_BWD_RECOMPUTE 2  /* upipe_attn_bwd with o_saved == NULL */
 #define UPIPE_PASS_FWD_PIPELINED 3  /* upipe_attn_fwd with pipelining enabled */
+#define UPIPE_PASS_BWD_PIPELINED 4  /* upipe_attn_bwd (o_saved given) with pipelining enabled */
 
 /*
  * Workspace size query.  Writes to *bytes the workspace that upipe_attn_fwd
  * (pass = UPIPE_PASS_FWD; UPIPE_PASS_FWD_PIPELINED while pipelining is
- * enabled), upipe_attn_bwd (pass = UPIPE_PASS_BWD) or upipe_attn_bwd in
- * full-recompute mode (pass = UPIPE_PASS_BWD_RECOMPUTE, projection mode only)
+ * enabled), upipe_attn_bwd (pass = UPIPE_PASS_BWD; UPIPE_PASS_BWD_PIPELINED
+ * while pipelining is enabled) or upipe_attn_bwd in full-recompute mode
+ * (pass = UPIPE_PASS_BWD_RECOMPUTE, projection mode only; never pipelined)
  * needs for these shapes.  The size is affine in head_chunk (per-chunk q-side buffers
  * plus the resident KV group): choosing head_chunk is how a caller fits the
  * layer into its memory budget (chunk-size ablation paragraph of the
@@ -202,7 +204,8 @@ int upipe_attn_fwd_static(int64_t seq_len, int32_t hidden, int32_t n_q_heads,
  *  dw_qkv   [(Hq+2Hkv)*head_dim, hidden] bf16 out, NULL iff hidden == 0
  *  dw_o     [hidden, Hq*head_dim] bf16 out, NULL iff hidden == 0
  *  workspace, workspace_bytes: at least the UPIPE_PASS_BWD query size
- *           (UPIPE_PASS_BWD_RECOMPUTE when o_saved is NULL)
+ *           (UPIPE_PASS_BWD_PIPELINED while pipelining is enabled,
+ *           UPIPE_PASS_BWD_RECOMPUTE when o_saved is NULL)
  */
 int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
                    int32_t head_dim, double rope_theta, int32_t head_chunk,
@@ -249,19 +252,27 @@ int upipe_profile_enable(int mask);
 int upipe_profile_read(int kind, double* total_ms, int64_t* launches);
 
 /*
- * Two-slot pipelining of the forward (off by default): chunk c+1's QKV
- * projection and RoPE/layout pass run on a second stream, into a second set
- * of q/k/v workspace buffers, while chunk c's attention runs on the caller's
- * stream (the overlap of the next group's projection with the current
- * group's attention, "Untied Ulysses Pushes Llama-3-8B Training to 5 Million
- * Tokens", Untied Ulysses section).  While enabled, upipe_attn_fwd needs the
- * UPIPE_PASS_FWD_PIPELINED workspace (else UPIPE_EWORKSPACE).  The stream
- * (default priority) and five events are created on a device's first
- * pipelined call and kept until the process ends; no device memory is
- * allocated.  Results are identical either way.  On one GPU the overlap
- * gains nothing measurable (the attention kernels keep every CU busy, so the
- * projection only takes CUs from them), hence off by default.  Process-wide
- * setting; returns UPIPE_OK.
+ * Two-slot pipelining (off by default): the next chunk's preparation runs on
+ * a second stream, into a second set of per-chunk workspace buffers, while
+ * the current chunk's attention runs on the caller's stream (the overlap of
+ * the next group's work with the current group's, "Untied Ulysses Pushes
+ * Llama-3-8B Training to 5 Million Tokens", Untied Ulysses section).
+ *   forward:  chunk c+1's QKV projection and RoPE/layout pass overlap chunk
+ *             c's attention (needs the UPIPE_PASS_FWD_PIPELINED workspace);
+ *   backward: chunk c+1's projection recompute, RoPE/layout pass, dO GEMM,
+ *             dW_o GEMM and dO preparation overlap chunk c's attention
+ *             backward and its dx / dW_qkv GEMMs (UPIPE_PASS_BWD_PIPELINED
+ *             workspace; the full-recompute backward, o_saved == NULL, keeps
+ *             the one-stream schedule).
+ * While enabled, the calls need those workspaces (else UPIPE_EWORKSPACE).
+ * The stream (default priority) and five events are created on a device's
+ * first pipelined call and kept until the process ends; no device memory is
+ * allocated.  Results are identical either way (the same kernels read the
+ * same inputs; only buffers and streams differ), except that the weight
+ * gradients' split-K fp32 atomics are order-dependent as in any two calls.
+ * On one GPU the overlap gains little (the attention kernels keep every CU
+ * busy, so the overlapped work mostly takes CUs from them), hence off by
+ * default.  Process-wide setting; returns UPIPE_OK.
  */
 int upipe_pipeline_enable(int on);
 

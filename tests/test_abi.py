@@ -70,8 +70,10 @@ def _ws(L, D, nq, nkv, d, hc, pss):
     ((1 << 24, 0, 64, 64, 128, 64, 0), B.UPIPE_EUNSUPPORTED),     # L_256 * kc = 2^30
     ((1 << 24, 32768, 8, 8, 128, 1, 0), B.UPIPE_EUNSUPPORTED),    # L_256 * hidden = 2^39
     ((4096, 1 << 22, 64, 64, 128, 64, 1), B.UPIPE_EUNSUPPORTED),  # hidden * w > 2^34
-    ((1024, 1024, 8, 2, 128, 2, 4), B.UPIPE_EINVAL),
+    ((1024, 1024, 8, 2, 128, 2, 5), B.UPIPE_EINVAL),
     ((1024, 1024, 8, 2, 128, 2, -1), B.UPIPE_EINVAL),
+    ((1024, 1024, 8, 2, 128, 2, 4), B.UPIPE_OK),             # pipelined backward
+    ((1024, 0, 8, 2, 128, 2, 4), B.UPIPE_OK),
     ((1024, 0, 8, 2, 128, 2, 3), B.UPIPE_OK),                # pipelined forward
     ((1024, 1024, 8, 2, 128, 2, 2), B.UPIPE_OK),             # recompute backward
     ((1024, 0, 8, 2, 128, 2, 2), B.UPIPE_EINVAL),            # ... needs projection mode
@@ -86,7 +88,8 @@ def test_workspace_query_null_output():
     assert rc == B.UPIPE_EINVAL
 
 
-@pytest.mark.parametrize("pss", [B.PASS_FWD, B.PASS_BWD, B.PASS_BWD_RECOMPUTE, B.PASS_FWD_PIPELINED])
+@pytest.mark.parametrize("pss", [B.PASS_FWD, B.PASS_BWD, B.PASS_BWD_RECOMPUTE, B.PASS_FWD_PIPELINED,
+                                 B.PASS_BWD_PIPELINED])
 @pytest.mark.parametrize("shape", [(262144, 5120, 8, 1), (524288, 0, 4, 1), (32768, 4096, 32, 8)])
 def test_workspace_affine_and_shrinking_in_chunk(shape, pss):
     L, D, nq, nkv = shape
@@ -254,6 +257,33 @@ def test_pipelined_forward_workspace_and_check():
         hc_amd.pipeline_enable(False)
     assert hc_amd.fwd_pass() == B.PASS_FWD
     assert _fwd(L=L, wsb=one - 1) == B.UPIPE_EWORKSPACE
+
+
+def test_pipelined_backward_workspace_and_check():
+    """The pipelined backward's second slot holds q [hc][Lp][128], k and v
+    [kc][Lp][128], dO [hc][Lp][128] (bf16), the LSE2 and D rows [hc][Lp]
+    (fp32), the staging block [L][(hc+2kc)128] (bf16) and the weight-gradient
+    accumulator [(hc+2kc)128][hidden] (fp32); while pipelining is enabled the
+    saved-output backward needs it and the recompute backward does not."""
+    L, D, hc, nq, nkv = 1000, 1024, 2, 8, 2
+    Lp, kc, w = 1024, 1, (2 + 2) * 128
+    up = lambda v: (v + 255) // 256 * 256
+    _, one = _ws(L, D, nq, nkv, 128, hc, B.PASS_BWD)
+    _, two = _ws(L, D, nq, nkv, 128, hc, B.PASS_BWD_PIPELINED)
+    assert two - one == (up(hc * Lp * 256) + 2 * up(kc * Lp * 256) + up(hc * Lp * 256)
+                         + 2 * up(hc * Lp * 4) + up(L * w * 2) + up(w * D * 4))
+    try:
+        hc_amd.pipeline_enable(True)
+        assert hc_amd.bwd_pass() == B.PASS_BWD_PIPELINED
+        assert hc_amd.bwd_pass(recompute=True) == B.PASS_BWD_RECOMPUTE
+        assert _bwd(L=L, wsb=one) == B.UPIPE_EWORKSPACE
+        assert _bwd(L=L, wsb=two, dx=None) == B.UPIPE_EINVAL
+        _, rec = _ws(L, D, nq, nkv, 128, hc, B.PASS_BWD_RECOMPUTE)
+        assert _bwd(L=L, wsb=rec - 1, o=None) == B.UPIPE_EWORKSPACE
+    finally:
+        hc_amd.pipeline_enable(False)
+    assert hc_amd.bwd_pass() == B.PASS_BWD
+    assert _bwd(L=L, wsb=one - 1) == B.UPIPE_EWORKSPACE
 
 
 def test_binding_refuses_host_tensors_before_any_call():

@@ -168,9 +168,9 @@ def test_qwen32b_share_full_length_chunk_sweep():
 
 
 def test_llama8b_layer_recompute_and_pipeline_modes():
-    """The benchmarked layer in the two optional modes.  The pipelined forward
-    gives the one-stream forward's bits.  The recompute backward gives the
-    saved-output backward's dx bits; its weight gradients are summed by
+    """The benchmarked layer in the optional modes.  The pipelined forward
+    gives the one-stream forward's bits.  The recompute and the pipelined
+    backward give the saved-output backward's dx bits; weight gradients are summed by
     split-K fp32 atomics in an order that varies from run to run, which moves
     a few bf16 values by one unit in the last place (2^-8 relative): they are
     held to 99.9% identical values and the relative L2 that a one-ulp change
@@ -201,11 +201,17 @@ def test_llama8b_layer_recompute_and_pipeline_modes():
     del piped
     ref = lib.attn_bwd(x, wq, wo, o, lse, dy, w.n_q, w.n_kv, hc, w.theta)
     rec = lib.attn_bwd(x, wq, wo, None, lse, dy, w.n_q, w.n_kv, hc, w.theta)
+    try:
+        lib.pipeline_enable(True)
+        pip = lib.attn_bwd(x, wq, wo, o, lse, dy, w.n_q, w.n_kv, hc, w.theta)
+    finally:
+        lib.pipeline_enable(False)
     torch.cuda.synchronize()
-    assert torch.equal(bits(ref[0]), bits(rec[0])), "dx"
-    for name, a, b in zip(("dw_qkv", "dw_o"), ref[1:], rec[1:]):
-        af, bf = a.float(), b.float()
-        rel = float(torch.linalg.vector_norm(af - bf) / torch.linalg.vector_norm(af))
-        same = float((bits(a) == bits(b)).float().mean())
-        print(f"{w.name}: recompute backward {name} rel-L2 {rel:.2e}, identical {same:.6f}", flush=True)
-        assert rel <= 2e-4 and same >= 0.999, name
+    for mode, res in (("recompute", rec), ("pipelined", pip)):
+        assert torch.equal(bits(ref[0]), bits(res[0])), (mode, "dx")
+        for name, a, b in zip(("dw_qkv", "dw_o"), ref[1:], res[1:]):
+            af, bf = a.float(), b.float()
+            rel = float(torch.linalg.vector_norm(af - bf) / torch.linalg.vector_norm(af))
+            same = float((bits(a) == bits(b)).float().mean())
+            print(f"{w.name}: {mode} backward {name} rel-L2 {rel:.2e}, identical {same:.6f}", flush=True)
+            assert rel <= 2e-4 and same >= 0.999, (mode, name)
