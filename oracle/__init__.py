@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for headwise-chunked causal GQA attention.
+"""fp64 CPU oracle for headwise-chunked causal GQA attention and the
+sequence-tiled SwiGLU MLP.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this package: only the tests, the smoke check of __graft_entry__ and the
@@ -16,3 +17,4 @@ from .attention import (  # noqa: F401
     rope,
     rope_angles,
 )
+from .mlp import mlp_bwd, mlp_fwd, silu, silu_grad  # noqa: F401

@@ -59,6 +59,47 @@ WORKLOADS = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class MlpWorkload:
+    """A sequence-tiled SwiGLU MLP shape: L rows of width hidden, ffn the
+    intermediate width, tile_rows the rows processed at a time."""
+
+    wid: int
+    name: str
+    L: int
+    hidden: int
+    ffn: int
+    tile_rows: int
+    x_sigma: float = 1.0
+    w_sigma: float = 0.02
+
+    def with_(self, **kw) -> "MlpWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# The Llama-3-8B MLP (hidden 4096, intermediate 14336) over the benchmarked
+# layer's sequence, and a small one for parity tests.
+MLP_WORKLOADS = {
+    11: MlpWorkload(11, "mlp_hidden512_ffn1536_L1000_tile256", 1000, 512, 1536, 256),
+    12: MlpWorkload(12, "llama3_8b_mlp_hidden4096_ffn14336_L32768_tile8192", 32768, 4096, 14336, 8192),
+}
+
+
+def make_mlp_inputs(w: MlpWorkload, with_grad: bool = True, seed_base: int | None = None) -> dict:
+    """bf16 bit arrays (uint16): x [L, hidden], w_gate_up [2 ffn, hidden] (gate
+    rows first), w_down [hidden, ffn], dy [L, hidden].  Seeds as for the
+    attention workloads (1000 * wid + tensor id)."""
+    base = 1000 * w.wid if seed_base is None else seed_base
+    out = {
+        "x": draw_bf16(base + TENSOR_IDS["x"], (w.L, w.hidden), w.x_sigma),
+        "w_gate_up": draw_bf16(base + TENSOR_IDS["w_qkv"], (2 * w.ffn, w.hidden), w.w_sigma),
+        "w_down": draw_bf16(base + TENSOR_IDS["w_o"], (w.hidden, w.ffn), w.w_sigma),
+    }
+    if with_grad:
+        out["dy"] = draw_bf16(base + TENSOR_IDS["dy"], (w.L, w.hidden), 1.0)
+    return out
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
