@@ -36,6 +36,10 @@ at every head chunk of its sweep.  Each entry gives ms per step, TFLOP/s, the
 dominant kernel's fraction of the bf16 peak, the planner's workspace and the
 allocator's peak, and the HBM rate of the RoPE / layout pass, the dO
 preparation and the dx accumulate (an epilogue of the dx GEMMs).
+
+mlp_workloads: the sequence-tiled SwiGLU MLP of the same training stack at
+the Llama-3-8B shape (hidden 4096, intermediate 14336) over L 32768, forward
++ backward at tiles of 2048, 8192 and 32768 rows.
 """
 from __future__ import annotations
 
@@ -331,6 +335,65 @@ def sweep(lib) -> dict:
     return out
 
 
+def mlp_sweep(lib) -> dict:
+    """The sequence-tiled SwiGLU MLP at the Llama-3-8B shape (hidden 4096,
+    intermediate 14336) over L 32768, forward + backward, at several tile
+    sizes: ms per step, TFLOP/s of model work (18 L hidden ffn: forward 6,
+    backward 12; the backward's recompute of the gate/up projection, 4 more,
+    is executed, not counted), workspace and allocator peak."""
+    import torch
+
+    import synthetic
+
+    base = synthetic.MLP_WORKLOADS[12]
+    out = {}
+    g = torch.Generator(device="cuda:0").manual_seed(1000 * base.wid)
+
+    def draw(shape, sigma):
+        t = torch.randn(*shape, generator=g, device="cuda:0", dtype=torch.float32)
+        if sigma != 1.0:
+            t.mul_(sigma)
+        return t.to(torch.bfloat16)
+
+    L, D, F = base.L, base.hidden, base.ffn
+    x, wgu, wd, dy = draw((L, D), 1.0), draw((2 * F, D), 0.02), draw((D, F), 0.02), draw((L, D), 1.0)
+    io = sum(t.numel() * t.element_size() for t in (x, wgu, wd, dy))
+    for tile in (2048, 8192, 32768):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        ws_f = lib.mlp_workspace_bytes(L, D, F, tile, lib.PASS_FWD)
+        ws_b = lib.mlp_workspace_bytes(L, D, F, tile, lib.PASS_BWD)
+        ws = torch.empty(max(ws_f, ws_b), dtype=torch.uint8, device="cuda:0")
+
+        def step():
+            lib.mlp_fwd(x, wgu, wd, tile, workspace=ws)
+            lib.mlp_bwd(x, wgu, wd, dy, tile, workspace=ws)
+
+        step()
+        torch.cuda.synchronize()
+        steps = 5
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        peak = torch.cuda.max_memory_allocated()
+        del ws
+        key = f"llama3_8b_mlp_hidden4096_ffn14336_L32768_tile{tile}"
+        out[key] = {
+            "seq_len": L, "hidden": D, "ffn": F, "tile_rows": tile, "steps": steps, "warmup": 1,
+            "ms_per_step": round(ms, 3),
+            "tflops": round(18.0 * L * D * F / (ms * 1e-3) / 1e12, 2),
+            "workspace_gib": {"fwd": round(ws_f / 2**30, 4), "bwd": round(ws_b / 2**30, 4)},
+            "peak_allocated_gib": round(peak / 2**30, 3),
+            "peak_allocated_minus_inputs_gib": round((peak - io) / 2**30, 3),
+        }
+        print(f"bench: {key}: {out[key]['ms_per_step']} ms/step, {out[key]['tflops']} TFLOP/s",
+              file=sys.stderr, flush=True)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -461,6 +524,7 @@ def main() -> int:
     if not args.no_sweep and not args.seq_len and args.workload == 2 and not args.chunk:
         del x, wq, wo, dy
         out["workloads"] = sweep(lib)
+        out["mlp_workloads"] = mlp_sweep(lib)
     if not args.no_cpu_baseline and not args.seq_len:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

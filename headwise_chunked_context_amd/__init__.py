@@ -1,7 +1,8 @@
-"""Headwise-chunked causal GQA attention (UPipe) for MI355X / gfx950.
+"""Headwise-chunked causal GQA attention (UPipe) for MI355X / gfx950, with the
+sequence-tiled SwiGLU MLP of the same long-context training stack.
 
-The layer runs in the HIP library libupipe_attn.so (C ABI in
-include/upipe_attn.h); this package is its thin ctypes binding.
+Both run in the HIP library libupipe_attn.so (C ABI in include/upipe_attn.h
+and include/upipe_mlp.h); this package is its thin ctypes binding.
 """
 from .binding import (  # noqa: F401
     EXPORTS,
@@ -26,6 +27,9 @@ from .binding import (  # noqa: F401
     fwd_pass,
     bwd_pass,
     lib,
+    mlp_bwd,
+    mlp_fwd,
+    mlp_workspace_bytes,
     pipeline_enable,
     profile_enable,
     profile_read,

@@ -28,12 +28,15 @@ PASS_FWD_PIPELINED = 3
 PASS_BWD_PIPELINED = 4
 _pipeline = False
 
-# names declared in include/upipe_attn.h
+# names declared in include/upipe_attn.h and include/upipe_mlp.h
 EXPORTS = (
     "upipe_attn_workspace_bytes",
     "upipe_attn_fwd",
     "upipe_attn_fwd_static",
     "upipe_attn_bwd",
+    "upipe_mlp_workspace_bytes",
+    "upipe_mlp_fwd",
+    "upipe_mlp_bwd",
     "upipe_profile_enable",
     "upipe_profile_read",
     "upipe_pipeline_enable",
@@ -77,6 +80,12 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_bwd.argtypes = [i64, i32, i32, i32, i32, f64, i32,
                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.upipe_attn_bwd.restype = ctypes.c_int
+    L.upipe_mlp_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.upipe_mlp_workspace_bytes.restype = ctypes.c_int
+    L.upipe_mlp_fwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.upipe_mlp_fwd.restype = ctypes.c_int
+    L.upipe_mlp_bwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.upipe_mlp_bwd.restype = ctypes.c_int
     L.upipe_strerror.argtypes = [ctypes.c_int]
     L.upipe_strerror.restype = ctypes.c_char_p
     L.upipe_version.argtypes = []
@@ -302,3 +311,61 @@ def attn_bwd(x, w_qkv, w_o, o_saved, lse, dy, n_q: int, n_kv: int, head_chunk: i
     if rc != UPIPE_OK:
         raise UpipeError(rc, "upipe_attn_bwd")
     return dx, dw_qkv, dw_o
+
+
+# ---------------------------------------------------------------- SwiGLU MLP
+def mlp_workspace_bytes(L: int, hidden: int, ffn: int, tile_rows: int, pass_: int) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().upipe_mlp_workspace_bytes(L, hidden, ffn, tile_rows, pass_, ctypes.byref(out))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_mlp_workspace_bytes")
+    return out.value
+
+
+def _check_mlp(x, w_gate_up, w_down):
+    import torch
+
+    bf = torch.bfloat16
+    if x is None or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor")
+    L, hidden = x.shape
+    if w_down is None or w_down.dim() != 2:
+        raise ValueError("w_down must be a 2-D tensor")
+    ffn = w_down.shape[1]
+    _check(x, "x", (L, hidden), bf)
+    _check(w_gate_up, "w_gate_up", (2 * ffn, hidden), bf, x.device)
+    _check(w_down, "w_down", (hidden, ffn), bf, x.device)
+    return L, hidden, ffn
+
+
+def mlp_fwd(x, w_gate_up, w_down, tile_rows: int, workspace=None, stream=None):
+    """Sequence-tiled SwiGLU MLP forward: y = (silu(x Wg^T) * x Wu^T) Wd^T,
+    w_gate_up = [Wg; Wu] (gate rows first).  Returns y."""
+    import torch
+
+    L, hidden, ffn = _check_mlp(x, w_gate_up, w_down)
+    y = torch.empty(L, hidden, dtype=torch.bfloat16, device=x.device)
+    ws = _workspace(mlp_workspace_bytes(L, hidden, ffn, tile_rows, PASS_FWD), x.device, workspace)
+    rc = lib().upipe_mlp_fwd(L, hidden, ffn, tile_rows, _ptr(x), _ptr(w_gate_up), _ptr(w_down),
+                             _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_mlp_fwd")
+    return y
+
+
+def mlp_bwd(x, w_gate_up, w_down, dy, tile_rows: int, workspace=None, stream=None):
+    """Backward of mlp_fwd.  Returns (dx, dw_gate_up, dw_down)."""
+    import torch
+
+    L, hidden, ffn = _check_mlp(x, w_gate_up, w_down)
+    _check(dy, "dy", (L, hidden), torch.bfloat16, x.device)
+    dx = torch.empty_like(x)
+    dwgu = torch.empty_like(w_gate_up)
+    dwd = torch.empty_like(w_down)
+    ws = _workspace(mlp_workspace_bytes(L, hidden, ffn, tile_rows, PASS_BWD), x.device, workspace)
+    rc = lib().upipe_mlp_bwd(L, hidden, ffn, tile_rows, _ptr(x), _ptr(w_gate_up), _ptr(w_down),
+                             _ptr(dy), _ptr(dx), _ptr(dwgu), _ptr(dwd), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_mlp_bwd")
+    return dx, dwgu, dwd

@@ -70,35 +70,6 @@ int check_shape(int64_t L, int32_t hidden, int32_t n_q, int32_t n_kv, int32_t he
   return UPIPE_OK;
 }
 
-// Split-K factor of the weight-gradient GEMMs (reduction over L).  The
-// 256 x 256 workgroups run one per CU, so with s splits the GEMM takes about
-// ceil(tiles*s / 256) rounds of ceil(L / (64 s)) k steps each, plus a fixed
-// cost per split for its fp32 atomic epilogue, about 5 k steps (fitted to
-// measurements of the layer's shapes).  Each split keeps at least 512 rows
-// of the sequence.
-int dw_splits(int64_t L, int M, int N) {
-  const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  int max_s = (int)((L + 511) / 512);
-  if (max_s > 32) max_s = 32;
-  if (max_s < 1) max_s = 1;
-  int best = 1;
-  int64_t best_cost = INT64_MAX;
-  for (int sp = 1; sp <= max_s; ++sp) {
-    const int64_t rounds = (tiles * sp + 255) / 256;
-    const int64_t steps = (L + 64LL * sp - 1) / (64LL * sp);
-    const int64_t cost = rounds * steps + 5LL * sp;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = sp;
-    }
-  }
-  return best;
-}
-int k_per_split(int64_t L, int splits) {
-  int64_t k = (L + splits - 1) / splits;
-  return (int)round_up64(k, 64);
-}
-
 // Workspace layout.  Every buffer that grows with the sequence is either
 // per q head of ONE chunk (hc) or per KV head a chunk touches (kc): the size
 // is affine in hc and independent of Hq.
@@ -771,7 +742,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       pd.do_ld = s.hc * d;
 
       // dW_o[:, cols] = dy^T O_c   (reduction over the sequence, split-K)
-      const int splits = dw_splits(s.L, s.D, s.hc * d);
+      const int splits = gemm_reduction_splits(s.L, s.D, s.hc * d);
       GemmArgs w;
       memset(&w, 0, sizeof(w));
       w.A = dy;
@@ -782,7 +753,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       w.M = s.D;
       w.N = s.hc * d;
       w.K = (int)s.L;
-      w.k_per_split = k_per_split(s.L, splits);
+      w.k_per_split = gemm_k_per_split(s.L, splits);
       UPIPE_TRY(timed(UPIPE_KERNEL_GEMM, sq, [&]() { return launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, sq); }));
       RowSegments ident;
       memset(&ident, 0, sizeof(ident));
@@ -871,7 +842,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       else
         UPIPE_LAUNCH(UPIPE_KERNEL_GEMM_ACCUM, launch_gemm(GEMM_NN, EPI_ACCUM_BF16, g, st));
 
-      const int splits = dw_splits(s.L, ncols, s.D);
+      const int splits = gemm_reduction_splits(s.L, ncols, s.D);
       GemmArgs w;
       memset(&w, 0, sizeof(w));
       w.A = staging[sl];
@@ -882,7 +853,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       w.M = ncols;
       w.N = s.D;
       w.K = (int)s.L;
-      w.k_per_split = k_per_split(s.L, splits);
+      w.k_per_split = gemm_k_per_split(s.L, splits);
       UPIPE_LAUNCH(UPIPE_KERNEL_GEMM, launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w, st));
       UPIPE_LAUNCH(UPIPE_KERNEL_FINALIZE, launch_acc_to_bf16(dw_acc[sl], ncols, s.D, dw_qkv, s.D, seg, st));
     }

@@ -33,6 +33,8 @@
 // Rows past M or N are read clamped (their products land in rows or columns
 // of C that are not stored); k rows past the end of a split are zeroed in
 // LDS after they land, so clamped reads never reach a stored result.
+#include <stdint.h>
+
 #include "kernels.h"
 
 namespace upipe {
@@ -503,6 +505,35 @@ hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, h
   }
 #undef UPIPE_GEMM_CASE
   return hipGetLastError();
+}
+
+// Split-K factor of a weight-gradient GEMM (reduction over K = L rows).  The
+// 256 x 256 workgroups run one per CU, so with s splits the GEMM takes about
+// ceil(tiles*s / 256) rounds of ceil(L / (64 s)) k steps each, plus a fixed
+// cost per split for its fp32 atomic epilogue, about 5 k steps (fitted to
+// measurements of the layer's shapes).  Each split keeps at least 512 rows.
+int gemm_reduction_splits(int64_t L, int M, int N) {
+  const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  int max_s = (int)((L + 511) / 512);
+  if (max_s > 32) max_s = 32;
+  if (max_s < 1) max_s = 1;
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int sp = 1; sp <= max_s; ++sp) {
+    const int64_t rounds = (tiles * sp + 255) / 256;
+    const int64_t steps = (L + 64LL * sp - 1) / (64LL * sp);
+    const int64_t cost = rounds * steps + 5LL * sp;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
+}
+
+int gemm_k_per_split(int64_t L, int splits) {
+  const int64_t k = (L + splits - 1) / splits;
+  return (int)((k + BK - 1) / BK * BK);
 }
 
 hipError_t launch_acc_to_bf16(float* acc, int M, int N, uint16_t* dst, int64_t ld_dst,

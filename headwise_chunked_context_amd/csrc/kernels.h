@@ -60,6 +60,11 @@ struct GemmArgs {
 
 hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, hipStream_t s);
 
+// Split count and k extent per split (a multiple of the k step) for a TN
+// GEMM reducing over L rows into an M x N fp32 accumulator (host side).
+int gemm_reduction_splits(int64_t L, int M, int N);
+int gemm_k_per_split(int64_t L, int splits);
+
 // fp32 accumulator [M][N] -> bf16 dst rows dst[map(m)*ld_dst + n]; clears the
 // accumulator for the next split-K GEMM.
 hipError_t launch_acc_to_bf16(float* acc, int M, int N, uint16_t* dst, int64_t ld_dst,

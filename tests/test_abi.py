@@ -12,7 +12,8 @@ import headwise_chunked_context_amd as hc_amd
 from headwise_chunked_context_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "upipe_attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 # fake, 256-byte aligned device addresses: never dereferenced by the host
 P = 0x7F0000000000
@@ -20,9 +21,11 @@ WS = 0x7F1000000000
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(upipe_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(upipe_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
