@@ -1,0 +1,75 @@
+"""CPU model of the storage roundings behind the widened intermediate gates.
+
+The saved O and the LSE are gated more loosely than the layer output
+(O: max-abs <= 2e-2 max(1, max|O|); LSE: 2e-2 + 2e-3 |LSE|).  This test shows
+that rounding alone reaches those sizes: the oracle's own per-head routines
+are evaluated on the operands the HIP path stores - the rotated q and k
+rounded to bf16, v rounded to fp16 (the forward's P V operand), all from
+bf16-rounded projections - and the result O rounded to bf16, with every
+other step exact in fp64.  Nothing of the HIP path is used; only where the
+roundings sit is taken from its storage formats.
+
+At the Llama-3-8B layer shape (hidden 4096, 32 q / 8 KV heads, chunk 8, short
+L) the model's saved-O error must reach a good part of the 2e-2 budget the
+plain gate would allow (so the plain gate would fail on rounding alone),
+while staying inside the widened one; the same for LSE."""
+import numpy as np
+
+import oracle
+import synthetic
+from oracle.attention import attention_fwd_head, rope
+
+
+def _bf16(a):
+    return synthetic.bf16_bits_to_f64(synthetic.f32_to_bf16_bits(np.asarray(a, dtype=np.float32)))
+
+
+def _f16(a):
+    return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def _model_o_lse(w, inp, n_heads):
+    """O and LSE of the first n_heads q heads with the storage roundings."""
+    d, G = w.head_dim, w.n_q // w.n_kv
+    x = synthetic.bf16_bits_to_f64(inp["x"])
+    wq = synthetic.bf16_bits_to_f64(inp["w_qkv"])
+    pos = np.arange(w.L)
+    o = np.zeros((w.L, n_heads * d))
+    lse = np.zeros((n_heads, w.L))
+    kv = {}
+    for h in range(n_heads):
+        g = h // G
+        if g not in kv:
+            kr = (w.n_q + g) * d
+            vr = (w.n_q + w.n_kv + g) * d
+            k = _bf16(rope(x @ wq[kr:kr + d].T, pos, w.theta))
+            v = _f16(_bf16(x @ wq[vr:vr + d].T))
+            kv = {g: (k, v)}
+        k, v = kv[g]
+        q = _bf16(rope(x @ wq[h * d:(h + 1) * d].T, pos, w.theta))
+        oh, lh = attention_fwd_head(q, k, v)
+        o[:, h * d:(h + 1) * d] = _bf16(oh)
+        lse[h] = lh
+    return o, lse
+
+
+def test_storage_roundings_alone_reach_the_intermediate_gates():
+    w = synthetic.WORKLOADS[2].with_(L=512)
+    inp = synthetic.make_inputs(w, with_grad=False)
+    nh = 8                                   # one chunk: two KV groups
+    x, wq, wo = (synthetic.bf16_bits_to_f64(inp[k]) for k in ("x", "w_qkv", "w_o"))
+    _, o_ref, lse_ref = oracle.layer_fwd(x, wq, wo, w.n_q, w.n_kv, w.head_dim, w.theta, 8)
+    o_ref, lse_ref = o_ref[:, : nh * w.head_dim], lse_ref[:nh]
+    o_mod, lse_mod = _model_o_lse(w, inp, nh)
+    o_err = float(np.abs(o_mod - o_ref).max())
+    o_gate = 2e-2 * max(1.0, float(np.abs(o_ref).max()))
+    lse_use = float(np.max(np.abs(lse_mod - lse_ref) / (2e-2 + 2e-3 * np.abs(lse_ref))))
+    print(f"rounding model: saved-O max-abs {o_err:.3e} (plain gate 2e-2, widened {o_gate:.3e}, "
+          f"max|O| {np.abs(o_ref).max():.2f}); LSE max-abs {np.abs(lse_mod - lse_ref).max():.3e}, "
+          f"widened gate used {lse_use:.2f}")
+    # rounding alone takes a good part of a plain 2e-2 budget on O, and puts
+    # LSE well past a 1e-3 gate ...
+    assert o_err > 0.5 * 2e-2
+    assert float(np.abs(lse_mod - lse_ref).max()) > 1e-3
+    # ... and stays inside the widened gates
+    assert o_err <= o_gate and lse_use <= 1.0
