@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     attn_fwd_static,
     fwd_pass,
     bwd_pass,
+    debug_enable,
     lib,
     mlp_bwd,
     mlp_fwd,

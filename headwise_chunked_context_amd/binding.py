@@ -40,6 +40,7 @@ EXPORTS = (
     "upipe_profile_enable",
     "upipe_profile_read",
     "upipe_pipeline_enable",
+    "upipe_debug_enable",
     "upipe_strerror",
     "upipe_version",
 )
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.upipe_profile_read.restype = ctypes.c_int
     L.upipe_pipeline_enable.argtypes = [ctypes.c_int]
     L.upipe_pipeline_enable.restype = ctypes.c_int
+    L.upipe_debug_enable.argtypes = [ctypes.c_int]
+    L.upipe_debug_enable.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -124,6 +127,14 @@ def pipeline_enable(on: bool) -> None:
     if rc != UPIPE_OK:
         raise UpipeError(rc, "upipe_pipeline_enable")
     _pipeline = bool(on)
+
+
+def debug_enable(on: bool) -> None:
+    """Debug mode: the library NaN-fills each chunk's (or MLP tile's)
+    workspace buffers before writing them, so stale reads show as NaN."""
+    rc = lib().upipe_debug_enable(1 if on else 0)
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_debug_enable")
 
 
 def fwd_pass() -> int:

@@ -20,6 +20,10 @@
 
 using namespace upipe;
 
+namespace upipe {
+bool g_debug_fill = false;
+}
+
 namespace {
 
 constexpr int64_t kMaxL = int64_t(1) << 24;
@@ -244,6 +248,12 @@ Side g_side[kMaxDevices];
 std::mutex g_side_mu;
 bool g_pipeline = false;
 
+// debug mode: NaN-fill (0xFF bytes) a buffer on the stream that will write it
+hipError_t debug_fill(void* p, size_t bytes, hipStream_t st) {
+  if (!g_debug_fill || !p) return hipSuccess;
+  return timed(UPIPE_KERNEL_FINALIZE, st, [&]() { return launch_fill(p, bytes, 0xFFFFFFFFu, st); });
+}
+
 int side_stream(Side** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return UPIPE_EHIP;
@@ -345,6 +355,11 @@ int upipe_pipeline_enable(int on) {
   return UPIPE_OK;
 }
 
+int upipe_debug_enable(int on) {
+  g_debug_fill = on != 0;
+  return UPIPE_OK;
+}
+
 int upipe_profile_enable(int mask) {
   if (mask < 0 || mask > UPIPE_PROFILE_ALL) return UPIPE_EINVAL;
   for (int k = 0; k < kKinds; ++k) {
@@ -442,6 +457,15 @@ int attn_fwd_run(const Shape& s, double rope_theta, const uint16_t* x, const uin
     uint16_t* k_rm = k_slot[kslot];
     uint16_t* v_rm = v_slot[kslot];
     if (side && c >= 2) UPIPE_TRY(hipStreamWaitEvent(sb, side->done[qslot], 0));
+    {
+      const size_t head_bytes = (size_t)s.Lp * d * 2;
+      if (staging) UPIPE_TRY(debug_fill(staging, (size_t)s.L * width * 2, sb));
+      UPIPE_TRY(debug_fill(q_rm, s.hc * head_bytes, sb));
+      if (ch.kv_first) {
+        UPIPE_TRY(debug_fill(k_rm, s.kc * head_bytes, sb));
+        UPIPE_TRY(debug_fill(v_rm, s.kc * head_bytes, sb));
+      }
+    }
     // 1. chunked QKV projection (or pick the given q/k/v columns) + RoPE
     PrepArgs pa;
     memset(&pa, 0, sizeof(pa));
@@ -652,6 +676,20 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   // output in recompute mode, dO, D and the base-2 LSE, and dW_o
   auto stage_prepare = [&](int c, int sl, int kl, hipStream_t sq) -> int {
     const Chunk ch = chunk_info(s, c);
+    if (g_debug_fill) {
+      const size_t head_bytes = (size_t)s.Lp * d * 2;
+      UPIPE_TRY(debug_fill(staging[sl], (size_t)s.L * width * 2, sq));
+      UPIPE_TRY(debug_fill(q_rm[sl], s.hc * head_bytes, sq));
+      UPIPE_TRY(debug_fill(do_rm[sl], s.hc * head_bytes, sq));
+      UPIPE_TRY(debug_fill(lse2[sl], (size_t)s.hc * s.Lp * 4, sq));
+      UPIPE_TRY(debug_fill(dvec[sl], (size_t)s.hc * s.Lp * 4, sq));
+      UPIPE_TRY(debug_fill(o_c, (size_t)s.L * s.hc * d * 2, sq));
+      if (ch.kv_first) {
+        UPIPE_TRY(debug_fill(k_rm[kl], s.kc * head_bytes, sq));
+        UPIPE_TRY(debug_fill(v_rm[kl], s.kc * head_bytes, sq));
+        UPIPE_TRY(debug_fill(v_t, s.kc * head_bytes, sq));
+      }
+    }
     // 1. recompute the chunk's rotated q (and k, v at a group start)
     PrepArgs pa;
     memset(&pa, 0, sizeof(pa));
@@ -773,6 +811,10 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
   // (dK/dV of the chunk's KV groups, dQ of its heads), then dx and dW_qkv
   auto stage_attend = [&](int c, int sl, int kl) -> int {
     const Chunk ch = chunk_info(s, c);
+    if (ch.kv_first) {  // the cross-chunk dK/dV accumulators start at this chunk
+      UPIPE_TRY(debug_fill(dk_acc, (size_t)s.kc * s.Lp * d * 4, st));
+      UPIPE_TRY(debug_fill(dv_acc, (size_t)s.kc * s.Lp * d * 4, st));
+    }
     // 3. attention backward: dK/dV of the chunk's KV groups, dQ of its heads
     BwdArgs ba;
     ba.q = q_rm[sl];

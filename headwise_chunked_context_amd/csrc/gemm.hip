@@ -351,8 +351,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   }
   __syncthreads();  // the epilogue reuses the stages
 
-  if (EPI == EPI_ATOMIC_F32) {
-    // split-K: every split adds its partial tile into one fp32 accumulator
+  if (EPI == EPI_ATOMIC_F32 || EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32) {
+    // fp32 accumulator [M][N]: split-K partial tiles meet by atomic adds; a
+    // single split owns its elements and stores (or adds) them plainly
     float* C = reinterpret_cast<float*>(p.C);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -362,7 +363,15 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = m0 + wm * (BM / WM) + mb * 16 + 4 * q4 + r;
-          if (m < p.M && n < p.N) atomicAdd(C + (int64_t)m * p.N + n, acc[mb][nb][r]);
+          if (m < p.M && n < p.N) {
+            float* c = C + (int64_t)m * p.N + n;
+            if (EPI == EPI_ATOMIC_F32)
+              atomicAdd(c, acc[mb][nb][r]);
+            else if (EPI == EPI_STORE_F32)
+              *c = acc[mb][nb][r];
+            else
+              *c += acc[mb][nb][r];
+          }
         }
       }
     return;
@@ -498,10 +507,15 @@ hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, h
       else if (epi == EPI_ACCUM_BF16) UPIPE_GEMM_CASE(true, false, EPI_ACCUM_BF16);
       else return hipErrorInvalidValue;
       break;
-    case GEMM_TN:
+    case GEMM_TN: {
+      // the plain fp32 epilogues need one writer per element: one split
+      const bool one_split = a.k_per_split >= a.K;
       if (epi == EPI_ATOMIC_F32) UPIPE_GEMM_CASE(false, false, EPI_ATOMIC_F32);
+      else if (epi == EPI_STORE_F32 && one_split) UPIPE_GEMM_CASE(false, false, EPI_STORE_F32);
+      else if (epi == EPI_ADD_F32 && one_split) UPIPE_GEMM_CASE(false, false, EPI_ADD_F32);
       else return hipErrorInvalidValue;
       break;
+    }
   }
 #undef UPIPE_GEMM_CASE
   return hipGetLastError();

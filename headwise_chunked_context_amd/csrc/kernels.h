@@ -23,7 +23,16 @@ struct RowSegments {
 };
 
 enum GemmLayout { GEMM_NT = 0, GEMM_NN = 1, GEMM_TN = 2 };
-enum GemmEpilogue { EPI_STORE_BF16 = 0, EPI_ACCUM_BF16 = 1, EPI_ATOMIC_F32 = 2 };
+// EPI_STORE_F32 / EPI_ADD_F32 write or add the fp32 tile into an [M][N]
+// accumulator with plain stores (TN only, one split: each element has one
+// writer); EPI_ATOMIC_F32 adds with atomics (any split count)
+enum GemmEpilogue {
+  EPI_STORE_BF16 = 0,
+  EPI_ACCUM_BF16 = 1,
+  EPI_ATOMIC_F32 = 2,
+  EPI_STORE_F32 = 3,
+  EPI_ADD_F32 = 4
+};
 
 struct GemmArgs {
   const uint16_t* A;
@@ -111,6 +120,11 @@ struct PrepDoutArgs {
 hipError_t launch_prep_dout(const PrepDoutArgs& a, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+// fills whole 16-byte chunks of [p, p + bytes) with a 32-bit pattern
+hipError_t launch_fill(void* p, size_t bytes, uint32_t pattern, hipStream_t s);
+// debug mode (upipe_debug_enable): workspace buffers are filled with 0xFF
+// bytes (NaN in bf16, fp16 and fp32) before each chunk or tile writes them
+extern bool g_debug_fill;
 
 // ---------------------------------------------------------- attention
 struct FwdArgs {

@@ -202,6 +202,24 @@ hipError_t launch_swiglu(bool bwd, uint16_t* gu, uint16_t* ad, int64_t rows, int
   return hipGetLastError();
 }
 
+// weight-gradient GEMM of one tile: acc[M][N] (+)= A^T B over `rows` rows
+hipError_t launch_dw(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* acc,
+                     int M, int N, int rows, bool first, hipStream_t st) {
+  GemmArgs g = gemm_args(A, lda, B, ldb, acc, 0, M, N, rows);
+  const int splits = gemm_reduction_splits(rows, M, N);
+  g.k_per_split = gemm_k_per_split(rows, splits);
+  const GemmEpilogue epi = splits > 1 ? EPI_ATOMIC_F32 : (first ? EPI_STORE_F32 : EPI_ADD_F32);
+  return launch_gemm(GEMM_TN, epi, g, st);
+}
+
+// debug mode: the tile's intermediates are NaN-filled before the tile
+hipError_t debug_fill_tile(uint16_t* gu, uint16_t* ad, const MlpShape& s, hipStream_t st) {
+  if (!g_debug_fill) return hipSuccess;
+  const hipError_t e = launch_fill(gu, (size_t)s.T * 2 * s.F * 2, 0xFFFFFFFFu, st);
+  if (e != hipSuccess) return e;
+  return launch_fill(ad, (size_t)s.T * s.F * 2, 0xFFFFFFFFu, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -235,6 +253,7 @@ int upipe_mlp_fwd(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t tile_row
   for (int64_t t0 = 0; t0 < s.L; t0 += s.T) {
     const int rows = (int)(s.L - t0 < s.T ? s.L - t0 : s.T);
     const uint16_t* xt = x + t0 * D;
+    UPIPE_TRY(debug_fill_tile(gu, ad, s, st));
     UPIPE_TRY(launch_gemm(GEMM_NT, EPI_STORE_BF16,
                           gemm_args(xt, D, w_gate_up, D, gu, 2 * F, rows, 2 * F, D), st));
     UPIPE_TRY(launch_swiglu(false, gu, ad, rows, F, st));
@@ -264,12 +283,19 @@ int upipe_mlp_bwd(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t tile_row
   float* acc_gu = at<float>(workspace, p.acc_gu);
   float* acc_down = at<float>(workspace, p.acc_down);
   const int D = s.D, F = s.F;
-  UPIPE_TRY(launch_zero(acc_gu, (size_t)2 * F * D * 4, st));
-  UPIPE_TRY(launch_zero(acc_down, (size_t)D * F * 4, st));
+  // the accumulators start at zero only if some tile's reduction is split
+  // (the first tile of a one-split reduction stores instead)
+  if (gemm_reduction_splits(s.T, 2 * F, D) > 1 || gemm_reduction_splits(s.T, D, F) > 1 ||
+      gemm_reduction_splits(s.L % s.T ? s.L % s.T : s.T, 2 * F, D) > 1 ||
+      gemm_reduction_splits(s.L % s.T ? s.L % s.T : s.T, D, F) > 1) {
+    UPIPE_TRY(launch_zero(acc_gu, (size_t)2 * F * D * 4, st));
+    UPIPE_TRY(launch_zero(acc_down, (size_t)D * F * 4, st));
+  }
   for (int64_t t0 = 0; t0 < s.L; t0 += s.T) {
     const int rows = (int)(s.L - t0 < s.T ? s.L - t0 : s.T);
     const uint16_t* xt = x + t0 * D;
     const uint16_t* dyt = dy + t0 * D;
+    UPIPE_TRY(debug_fill_tile(gu, ad, s, st));
     // recompute h | u, then da = dy_t W_down
     UPIPE_TRY(launch_gemm(GEMM_NT, EPI_STORE_BF16,
                           gemm_args(xt, D, w_gate_up, D, gu, 2 * F, rows, 2 * F, D), st));
@@ -279,13 +305,13 @@ int upipe_mlp_bwd(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t tile_row
     // dx_t = [dh | du] [W_gate; W_up]
     UPIPE_TRY(launch_gemm(GEMM_NN, EPI_STORE_BF16,
                           gemm_args(gu, 2 * F, w_gate_up, D, dx + t0 * D, D, rows, D, 2 * F), st));
-    // dW_gate_up += [dh | du]^T x_t ;  dW_down += dy_t^T a
-    GemmArgs w1 = gemm_args(gu, 2 * F, xt, D, acc_gu, 0, 2 * F, D, rows);
-    w1.k_per_split = gemm_k_per_split(rows, gemm_reduction_splits(rows, 2 * F, D));
-    UPIPE_TRY(launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w1, st));
-    GemmArgs w2 = gemm_args(dyt, D, ad, F, acc_down, 0, D, F, rows);
-    w2.k_per_split = gemm_k_per_split(rows, gemm_reduction_splits(rows, D, F));
-    UPIPE_TRY(launch_gemm(GEMM_TN, EPI_ATOMIC_F32, w2, st));
+    // dW_gate_up += [dh | du]^T x_t ;  dW_down += dy_t^T a.  A tile's GEMM
+    // whose reduction is one split owns every accumulator element: the first
+    // tile stores, later ones add, both with plain stores (the tiles run in
+    // order on one stream); split reductions add with atomics into the
+    // accumulators cleared above
+    UPIPE_TRY(launch_dw(gu, 2 * F, xt, D, acc_gu, 2 * F, D, rows, t0 == 0, st));
+    UPIPE_TRY(launch_dw(dyt, D, ad, F, acc_down, D, F, rows, t0 == 0, st));
   }
   RowSegments ident;
   memset(&ident, 0, sizeof(ident));

@@ -150,10 +150,12 @@ __global__ __launch_bounds__(256) void prep_dout_kernel(PrepDoutArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(u32x4* p, int64_t n16) {
+// fills n16 16-byte chunks with a 32-bit pattern (0: the accumulator
+// clears; 0xFFFFFFFF: debug mode's NaN fill)
+__global__ __launch_bounds__(256) void zero_kernel(u32x4* p, int64_t n16, uint32_t pattern) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   int64_t stride = (int64_t)gridDim.x * 256;
-  for (; i < n16; i += stride) p[i] = u32x4{0, 0, 0, 0};
+  for (; i < n16; i += stride) p[i] = u32x4{pattern, pattern, pattern, pattern};
 }
 
 }  // namespace
@@ -170,14 +172,16 @@ hipError_t launch_prep_dout(const PrepDoutArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+hipError_t launch_fill(void* p, size_t bytes, uint32_t pattern, hipStream_t s) {
   int64_t n16 = (int64_t)(bytes / 16);
   if (n16 == 0) return hipSuccess;
   int64_t blocks = (n16 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     reinterpret_cast<u32x4*>(p), n16);
+                     reinterpret_cast<u32x4*>(p), n16, pattern);
   return hipGetLastError();
 }
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) { return launch_fill(p, bytes, 0u, s); }
 
 }  // namespace upipe

@@ -276,6 +276,21 @@ int upipe_profile_read(int kind, double* total_ms, int64_t* launches);
  */
 int upipe_pipeline_enable(int on);
 
+/*
+ * Debug mode (off by default), a check for workspace reuse between chunks:
+ * before each chunk (and each tile of upipe_mlp_fwd / upipe_mlp_bwd) the
+ * library fills that chunk's workspace buffers with 0xFF bytes (NaN in
+ * bf16, fp16 and fp32) by a fill kernel on the stream that then writes
+ * them, so a kernel that read a buffer before the chunk wrote it, or read a
+ * previous chunk's leftovers, would turn results into NaN.  Buffers that
+ * legitimately carry state across chunks (a KV group's k, v and dK/dV
+ * accumulators while the group spans chunks, the weight-gradient
+ * accumulators) are filled when that state begins.  Results are identical
+ * with and without it; it costs extra HBM writes.  Process-wide setting;
+ * returns UPIPE_OK.
+ */
+int upipe_debug_enable(int on);
+
 /* Static, human-readable text for a status code.  Never NULL. */
 const char* upipe_strerror(int status);
 

@@ -363,3 +363,10 @@ def test_static_scratch_limit_covers_the_benchmarked_forward():
     chunk 16 does not."""
     assert _ws(32768, 4096, 32, 8, 128, 8, B.PASS_FWD)[1] <= B.STATIC_SCRATCH_BYTES
     assert _ws(32768, 4096, 32, 8, 128, 16, B.PASS_FWD)[1] > B.STATIC_SCRATCH_BYTES
+
+
+def test_debug_mode_switch_is_host_only():
+    """upipe_debug_enable only sets host state (no GPU here)."""
+    L = B.lib()
+    assert L.upipe_debug_enable(1) == B.UPIPE_OK
+    assert L.upipe_debug_enable(0) == B.UPIPE_OK

@@ -150,3 +150,25 @@ def test_llama8b_mlp_full_length_sampled_rows():
     assert errs["dwgu_vs_one_tile"] <= 1e-3 and errs["dwd_vs_one_tile"] <= 1e-3
     for k in ("y", "dx"):
         assert torch.equal(g[k].view(torch.int16), one[k].view(torch.int16)), k
+
+
+def test_debug_nan_fill_changes_nothing():
+    """Debug mode NaN-fills each tile's intermediates before the tile: the
+    results must equal the normal run's (y and dx bit for bit; the weight
+    gradients to their fp32 summation order)."""
+    import headwise_chunked_context_amd as lib
+
+    torch = _torch()
+    w = synthetic.MLP_WORKLOADS[11].with_(L=777, tile_rows=200)
+    inp = synthetic.make_mlp_inputs(w)
+    ref = run_gpu(inp, w.tile_rows)
+    try:
+        lib.debug_enable(True)
+        dbg = run_gpu(inp, w.tile_rows)
+    finally:
+        lib.debug_enable(False)
+    for k in ("y", "dx"):
+        assert torch.equal(ref[k].view(torch.int16), dbg[k].view(torch.int16)), k
+    for k in ("dwgu", "dwd"):
+        assert np.isfinite(from_dev_bf16(dbg[k])).all()
+        assert rel_l2(from_dev_bf16(dbg[k]), from_dev_bf16(ref[k])) <= 1e-3, k
