@@ -161,6 +161,22 @@ def copy_calibration() -> None:
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
+def executed_mfma_flops_per_step(w) -> dict:
+    """MFMA FLOPs each kernel class executes per step (recomputation included):
+    the attention forward 4 d P Hq, dK/dV 8 d P Hq, dQ 6 d P Hq (its S and dP
+    again), the GEMMs the model's projection FLOPs plus the backward's
+    recompute of the QKV projection, 2 L hidden (Hq + 2 Hkv) d."""
+    d = w.head_dim
+    P = w.L * (w.L + 1) / 2
+    out = {"attn_fwd": 4.0 * d * P * w.n_q, "attn_bwd_dkdv": 8.0 * d * P * w.n_q,
+           "attn_bwd_dq": 6.0 * d * P * w.n_q}
+    if w.projection:
+        acc = gemm_accum_flops_per_step(w)
+        out["gemm"] = gemm_flops_per_step(w) - acc + 2.0 * w.L * w.hidden * (w.n_q + 2 * w.n_kv) * d
+        out["gemm_accum"] = acc
+    return out
+
+
 def hbm_bytes_per_step(w) -> dict:
     """Algorithmic HBM bytes per step of the passes that move data rather than
     contract it, for the classes the library times separately:
@@ -477,6 +493,11 @@ def main() -> int:
             algo_flops_per_launch(w, "attn_fwd") / (prof_all["attn_fwd"][0] / nf * 1e-3) / 1e12, 2)
     breakdown = {k: {"ms_per_step": round(v[0] / prof_steps, 3), "launches_per_step": v[1] // prof_steps}
                  for k, v in prof_all.items()}
+    # MFMA utilisation per class: executed MFMA FLOPs over the class's
+    # event-timed time at the bf16 peak (the rocprofv3 ratio
+    # SQ_VALU_MFMA_BUSY_CYCLES / SIMD-cycles at 2.4 GHz, from the timing)
+    mfma_util = {k: round(f / (prof_all[k][0] / prof_steps * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4)
+                 for k, f in executed_mfma_flops_per_step(w).items() if prof_all[k][0] > 0}
 
     chunks = [c for c in range(1, w.n_q + 1)
               if w.n_q % c == 0 and (c % (w.n_q // w.n_kv) == 0 or (w.n_q // w.n_kv) % c == 0)]
@@ -514,6 +535,7 @@ def main() -> int:
         "model_flops_per_step": flops,
         "roofline": roofline,
         "kernel_breakdown": breakdown,
+        "mfma_util": mfma_util,
         "kernel_breakdown_from": ("the last warm-up step, every kernel class timed" if prof_steps == 1
                                   else "the timed steps, every kernel class timed"),
         "workspace_gib": {"fwd": round(ws_f / 2**30, 4), "bwd": round(ws_b / 2**30, 4),
