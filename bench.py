@@ -31,8 +31,10 @@ layer shape at a short sequence), reported in the same unit.
 workloads: every other layer shape the metric is quoted on, each timed the
 same way for a few steps on inputs drawn on the device (same distributions as
 the seeded host recipe): the small GQA layer, the two one-GPU shares of the
-Llama-3-8B model (q/k/v given, L 524288 and 1048576) and the 32B-class share
-at every head chunk of its sweep.  Each entry gives ms per step, TFLOP/s, the
+Llama-3-8B model (q/k/v given, L 524288 and 1048576), the 32B-class share
+at every head chunk of its sweep (with and without the two-slot pipeline),
+and the benchmarked layer with the full-recompute backward and with the
+pipeline.  Each entry gives ms per step, TFLOP/s, the
 dominant kernel's fraction of the bf16 peak, the planner's workspace and the
 allocator's peak, and the HBM rate of the RoPE / layout pass, the dO
 preparation and the dx accumulate (an epilogue of the dx GEMMs).
@@ -312,14 +314,20 @@ def sweep(lib) -> dict:
 
     W = synthetic.WORKLOADS
     plan = [(W[1], 3, 10, False), (W[3], 1, 2, False), (W[5], 1, 1, False)]
+    # the benchmarked layer in its optional modes: full recompute (o_saved
+    # NULL) and the two-slot pipeline
+    plan += [(W[2], 1, 3, "recompute"), (W[2], 1, 3, True)]
     # the 32B-class share at every chunk of its sweep, on one stream and with
     # the two-slot pipeline (next chunk's preparation on a second stream)
     plan += [(W[4].with_(head_chunk=c), 1, 2, pipe) for pipe in (False, True) for c in (1, 2, 4, 8)]
     out = {}
-    for w, warmup, steps, pipe in plan:
+    for w, warmup, steps, mode in plan:
+        pipe, recompute = mode is True, mode == "recompute"
         key = w.name if w.wid != 4 else f"{w.name}_chunk{w.head_chunk}"
         if pipe:
             key += "_pipelined"
+        if recompute:
+            key += "_recompute"
         torch.cuda.empty_cache()
         x, wq, wo, dy = device_inputs(w, seed=1000 * w.wid)
         torch.cuda.synchronize()
@@ -327,7 +335,7 @@ def sweep(lib) -> dict:
         torch.cuda.reset_peak_memory_stats()   # the layer's own peak, not the draw's
         lib.pipeline_enable(pipe)
         try:
-            r = time_layer(lib, w, x, wq, wo, dy, steps, warmup)
+            r = time_layer(lib, w, x, wq, wo, dy, steps, warmup, recompute=recompute)
         finally:
             lib.pipeline_enable(False)
         peak = torch.cuda.max_memory_allocated()
@@ -336,7 +344,9 @@ def sweep(lib) -> dict:
         flops = model_flops(w)
         out[key] = {
             "seq_len": w.L, "hidden": w.hidden, "n_q_heads": w.n_q, "n_kv_heads": w.n_kv,
-            "head_chunk": w.head_chunk, "pipeline": pipe, "steps": steps, "warmup": warmup,
+            "head_chunk": w.head_chunk, "pipeline": pipe,
+            "backward": "recompute attention output" if recompute else "saved attention output",
+            "steps": steps, "warmup": warmup,
             "ms_per_step": round(r["ms"], 3),
             "tflops": round(flops / (r["ms"] * 1e-3) / 1e12, 2),
             "roofline_kernel": r["dom"],
