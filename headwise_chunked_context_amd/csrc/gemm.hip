@@ -352,8 +352,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   __syncthreads();  // the epilogue reuses the stages
 
   if (EPI == EPI_ATOMIC_F32 || EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32) {
-    // fp32 accumulator [M][N]: split-K partial tiles meet by atomic adds; a
-    // single split owns its elements and stores (or adds) them plainly
+    // fp32 accumulator [M][N]: split-K partial tiles meet by atomic adds, or
+    // each split stores its partial tile into its own [M][N] slice (summed
+    // in split order afterwards); a single split owns its elements and may
+    // also add them plainly
     float* C = reinterpret_cast<float*>(p.C);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -364,7 +366,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
         for (int r = 0; r < 4; ++r) {
           const int m = m0 + wm * (BM / WM) + mb * 16 + 4 * q4 + r;
           if (m < p.M && n < p.N) {
-            float* c = C + (int64_t)m * p.N + n;
+            // EPI_STORE_F32 writes split s's partial tile into slice s
+            float* c = C + (int64_t)m * p.N + n +
+                       (EPI == EPI_STORE_F32 ? (int64_t)(tile / (gx * gy)) * p.M * p.N : 0);
             if (EPI == EPI_ATOMIC_F32)
               atomicAdd(c, acc[mb][nb][r]);
             else if (EPI == EPI_STORE_F32)
@@ -487,11 +491,44 @@ __global__ __launch_bounds__(256) void acc_to_bf16_kernel(float* acc, int M, int
   *reinterpret_cast<u32x4*>(dst + row * ld + n) = out;
 }
 
+// dst[m][n] (bf16) = sum over s of slices[s][m][n] (fp32), added in slice
+// order, so the result does not depend on which split finished first
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* slices, int nslices, int M,
+                                                         int N, uint16_t* dst, int64_t ld) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 8-wide chunk each
+  const int64_t chunks = (int64_t)M * (N / 8);
+  if (idx >= chunks) return;
+  const int m = (int)(idx / (N / 8));
+  const int n = (int)(idx % (N / 8)) * 8;
+  f32x4 a = f32x4{0, 0, 0, 0}, b = f32x4{0, 0, 0, 0};
+  for (int sl = 0; sl < nslices; ++sl) {
+    const float* src = slices + (int64_t)sl * M * N + (int64_t)m * N + n;
+    a += *reinterpret_cast<const f32x4*>(src);
+    b += *reinterpret_cast<const f32x4*>(src + 4);
+  }
+  u32x4 out;
+  out[0] = pack_bf16x2(a[0], a[1]);
+  out[1] = pack_bf16x2(a[2], a[3]);
+  out[2] = pack_bf16x2(b[0], b[1]);
+  out[3] = pack_bf16x2(b[2], b[3]);
+  *reinterpret_cast<u32x4*>(dst + (int64_t)m * ld + n) = out;
+}
+
 }  // namespace
 
+hipError_t launch_sum_slices(const float* slices, int nslices, int M, int N, uint16_t* dst,
+                             int64_t ld, hipStream_t s) {
+  const int64_t chunks = (int64_t)M * (N / 8);
+  dim3 grid((unsigned)((chunks + 255) / 256));
+  hipLaunchKernelGGL(sum_slices_kernel, grid, dim3(256), 0, s, slices, nslices, M, N, dst, ld);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, hipStream_t s) {
-  // k steps of BK must not read past a k-contiguous row, nor splits overlap
+  // k steps of BK must not read past a k-contiguous row, nor splits overlap;
+  // only the atomic epilogue may combine several splits
   if (a.k_per_split % BK != 0 || (layout != GEMM_TN && a.K % BK != 0)) return hipErrorInvalidValue;
+  if (epi != EPI_ATOMIC_F32 && epi != EPI_STORE_F32 && a.k_per_split < a.K) return hipErrorInvalidValue;
   dim3 grid((unsigned)(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM) *
                        ((a.K + a.k_per_split - 1) / a.k_per_split)));
   dim3 block(NT);
@@ -500,22 +537,23 @@ hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, h
     case GEMM_NT:
       if (epi == EPI_STORE_BF16) UPIPE_GEMM_CASE(true, true, EPI_STORE_BF16);
       else if (epi == EPI_ACCUM_BF16) UPIPE_GEMM_CASE(true, true, EPI_ACCUM_BF16);
+      else if (epi == EPI_ATOMIC_F32) UPIPE_GEMM_CASE(true, true, EPI_ATOMIC_F32);
+      else if (epi == EPI_STORE_F32) UPIPE_GEMM_CASE(true, true, EPI_STORE_F32);
       else return hipErrorInvalidValue;
       break;
     case GEMM_NN:
       if (epi == EPI_STORE_BF16) UPIPE_GEMM_CASE(true, false, EPI_STORE_BF16);
       else if (epi == EPI_ACCUM_BF16) UPIPE_GEMM_CASE(true, false, EPI_ACCUM_BF16);
+      else if (epi == EPI_ATOMIC_F32) UPIPE_GEMM_CASE(true, false, EPI_ATOMIC_F32);
+      else if (epi == EPI_STORE_F32) UPIPE_GEMM_CASE(true, false, EPI_STORE_F32);
       else return hipErrorInvalidValue;
       break;
-    case GEMM_TN: {
-      // the plain fp32 epilogues need one writer per element: one split
-      const bool one_split = a.k_per_split >= a.K;
+    case GEMM_TN:
       if (epi == EPI_ATOMIC_F32) UPIPE_GEMM_CASE(false, false, EPI_ATOMIC_F32);
-      else if (epi == EPI_STORE_F32 && one_split) UPIPE_GEMM_CASE(false, false, EPI_STORE_F32);
-      else if (epi == EPI_ADD_F32 && one_split) UPIPE_GEMM_CASE(false, false, EPI_ADD_F32);
+      else if (epi == EPI_STORE_F32) UPIPE_GEMM_CASE(false, false, EPI_STORE_F32);
+      else if (epi == EPI_ADD_F32) UPIPE_GEMM_CASE(false, false, EPI_ADD_F32);
       else return hipErrorInvalidValue;
       break;
-    }
   }
 #undef UPIPE_GEMM_CASE
   return hipGetLastError();

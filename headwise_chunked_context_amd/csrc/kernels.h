@@ -23,9 +23,10 @@ struct RowSegments {
 };
 
 enum GemmLayout { GEMM_NT = 0, GEMM_NN = 1, GEMM_TN = 2 };
-// EPI_STORE_F32 / EPI_ADD_F32 write or add the fp32 tile into an [M][N]
-// accumulator with plain stores (TN only, one split: each element has one
-// writer); EPI_ATOMIC_F32 adds with atomics (any split count)
+// EPI_STORE_F32 writes each split's fp32 partial tile into its own [M][N]
+// slice of C (slice s at C + s*M*N; one split: C itself); EPI_ADD_F32 adds
+// the fp32 tile into C with plain stores (TN, one split: each element has
+// one writer); EPI_ATOMIC_F32 adds with atomics (any split count)
 enum GemmEpilogue {
   EPI_STORE_BF16 = 0,
   EPI_ACCUM_BF16 = 1,
@@ -68,6 +69,11 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, hipStream_t s);
+
+// bf16 dst rows = the sum of nslices fp32 [M][N] slices, in slice order
+// (the partial results of a GEMM whose splits store into their own slices)
+hipError_t launch_sum_slices(const float* slices, int nslices, int M, int N, uint16_t* dst,
+                             int64_t ld, hipStream_t s);
 
 // Split count and k extent per split (a multiple of the k step) for a TN
 // GEMM reducing over L rows into an M x N fp32 accumulator (host side).

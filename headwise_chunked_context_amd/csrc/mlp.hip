@@ -128,9 +128,25 @@ int check_mlp_shape(int64_t L, int32_t hidden, int32_t ffn, int32_t tile_rows, M
   return UPIPE_OK;
 }
 
+// A GEMM whose output is hidden wide ([T, hidden]: the down projection and
+// dx) has only ceil(T/256) * ceil(hidden/256) workgroups of 256 x 256; below
+// one per CU its reduction is split so the chip fills, each split storing
+// its fp32 partial result into its own [T, hidden] slice, and the slices are
+// summed in split order into the bf16 output (the same bits every run).
+constexpr int kCUs = 256;
+int out_splits(const MlpShape& s, int K) {
+  const int64_t tiles = (int64_t)((s.T + 255) / 256) * ((s.D + 255) / 256);
+  if (tiles >= kCUs) return 1;
+  int sp = (int)((kCUs + tiles - 1) / tiles);
+  const int max_sp = K / 512;  // each split keeps at least 8 k steps
+  if (sp > max_sp) sp = max_sp;
+  return sp < 1 ? 1 : sp;
+}
+
 struct MlpPlan {
   size_t gu;        // [T][2F] bf16: h | u, then dh | du
   size_t ad;        // [T][F] bf16: a (forward), da then a (backward)
+  size_t acc_out;   // [splits][T][D] fp32: the split hidden-wide GEMM's partial results
   size_t acc_gu;    // [2F][D] fp32 dW_gate_up accumulator (backward)
   size_t acc_down;  // [D][F] fp32 dW_down accumulator (backward)
   size_t total;
@@ -147,6 +163,9 @@ MlpPlan make_mlp_plan(const MlpShape& s, int pass) {
   const size_t T = (size_t)s.T, D = (size_t)s.D, F = (size_t)s.F;
   p.gu = take(T * 2 * F * 2);
   p.ad = take(T * F * 2);
+  const int K = pass == UPIPE_PASS_BWD ? 2 * s.F : s.F;
+  const int sp = out_splits(s, K);
+  p.acc_out = sp > 1 ? take((size_t)sp * T * D * 4) : (size_t)-1;
   if (pass == UPIPE_PASS_BWD) {
     p.acc_gu = take(2 * F * D * 4);
     p.acc_down = take(D * F * 4);
@@ -202,6 +221,22 @@ hipError_t launch_swiglu(bool bwd, uint16_t* gu, uint16_t* ad, int64_t rows, int
   return hipGetLastError();
 }
 
+// hidden-wide GEMM of one tile, out[rows][D] = A B (layout NT or NN, K the
+// reduction): one split stores bf16 directly; several store fp32 slices that
+// are then summed in order into out
+hipError_t launch_out(GemmLayout layout, const uint16_t* A, int64_t lda, const uint16_t* B,
+                      int64_t ldb, uint16_t* out, int rows, int D, int K, int splits, float* acc,
+                      hipStream_t st) {
+  if (splits <= 1)
+    return launch_gemm(layout, EPI_STORE_BF16, gemm_args(A, lda, B, ldb, out, D, rows, D, K), st);
+  GemmArgs g = gemm_args(A, lda, B, ldb, acc, 0, rows, D, K);
+  g.k_per_split = gemm_k_per_split(K, splits);
+  const int used = (K + g.k_per_split - 1) / g.k_per_split;  // splits the GEMM launches
+  hipError_t e = launch_gemm(layout, EPI_STORE_F32, g, st);
+  if (e != hipSuccess) return e;
+  return launch_sum_slices(acc, used, rows, D, out, D, st);
+}
+
 // weight-gradient GEMM of one tile: acc[M][N] (+)= A^T B over `rows` rows
 hipError_t launch_dw(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* acc,
                      int M, int N, int rows, bool first, hipStream_t st) {
@@ -249,7 +284,9 @@ int upipe_mlp_fwd(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t tile_row
   const MlpPlan p = make_mlp_plan(s, UPIPE_PASS_FWD);
   uint16_t* gu = at<uint16_t>(workspace, p.gu);
   uint16_t* ad = at<uint16_t>(workspace, p.ad);
+  float* acc_out = at<float>(workspace, p.acc_out);
   const int D = s.D, F = s.F;
+  const int splits = acc_out ? out_splits(s, F) : 1;
   for (int64_t t0 = 0; t0 < s.L; t0 += s.T) {
     const int rows = (int)(s.L - t0 < s.T ? s.L - t0 : s.T);
     const uint16_t* xt = x + t0 * D;
@@ -257,8 +294,7 @@ int upipe_mlp_fwd(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t tile_row
     UPIPE_TRY(launch_gemm(GEMM_NT, EPI_STORE_BF16,
                           gemm_args(xt, D, w_gate_up, D, gu, 2 * F, rows, 2 * F, D), st));
     UPIPE_TRY(launch_swiglu(false, gu, ad, rows, F, st));
-    UPIPE_TRY(launch_gemm(GEMM_NT, EPI_STORE_BF16,
-                          gemm_args(ad, F, w_down, F, y + t0 * D, D, rows, D, F), st));
+    UPIPE_TRY(launch_out(GEMM_NT, ad, F, w_down, F, y + t0 * D, rows, D, F, splits, acc_out, st));
   }
   return UPIPE_OK;
 }
@@ -282,7 +318,9 @@ int upipe_mlp_bwd(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t tile_row
   uint16_t* ad = at<uint16_t>(workspace, p.ad);
   float* acc_gu = at<float>(workspace, p.acc_gu);
   float* acc_down = at<float>(workspace, p.acc_down);
+  float* acc_out = at<float>(workspace, p.acc_out);
   const int D = s.D, F = s.F;
+  const int splits = acc_out ? out_splits(s, 2 * F) : 1;
   // the accumulators start at zero only if some tile's reduction is split
   // (the first tile of a one-split reduction stores instead)
   if (gemm_reduction_splits(s.T, 2 * F, D) > 1 || gemm_reduction_splits(s.T, D, F) > 1 ||
@@ -303,8 +341,8 @@ int upipe_mlp_bwd(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t tile_row
                           gemm_args(dyt, D, w_down, F, ad, F, rows, F, D), st));
     UPIPE_TRY(launch_swiglu(true, gu, ad, rows, F, st));
     // dx_t = [dh | du] [W_gate; W_up]
-    UPIPE_TRY(launch_gemm(GEMM_NN, EPI_STORE_BF16,
-                          gemm_args(gu, 2 * F, w_gate_up, D, dx + t0 * D, D, rows, D, 2 * F), st));
+    UPIPE_TRY(launch_out(GEMM_NN, gu, 2 * F, w_gate_up, D, dx + t0 * D, rows, D, 2 * F, splits,
+                         acc_out, st));
     // dW_gate_up += [dh | du]^T x_t ;  dW_down += dy_t^T a.  A tile's GEMM
     // whose reduction is one split owns every accumulator element: the first
     // tile stores, later ones add, both with plain stores (the tiles run in

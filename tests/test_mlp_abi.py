@@ -19,15 +19,27 @@ def _ws(L, D, F, T, pss):
 
 
 def test_workspace_is_one_tile_of_intermediates_plus_weight_accumulators():
-    """Forward: [T, 2F] (h | u) and [T, F] (a) bf16; backward adds the fp32
-    gradient accumulators of both weights (12 D F bytes), independent of L
-    and T.  A tile longer than the sequence is the sequence."""
+    """Forward: [T, 2F] (h | u) and [T, F] (a) bf16, plus s fp32 [T, D]
+    slices when the tile is too short for the hidden-wide GEMMs (output
+    [T, D], reduction K = F forward, 2F backward) to fill 256 CUs with
+    256 x 256 output tiles: their reduction is split in s = min(ceil(256 /
+    tiles), K / 512) parts.  The backward adds the fp32 gradient
+    accumulators of both weights (12 D F bytes), independent of L and T.  A
+    tile longer than the sequence is the sequence."""
     up = lambda v: (v + 255) // 256 * 256
     L, D, F = 32768, 4096, 14336
+
+    def slices(T, K):
+        tiles = -(-T // 256) * -(-D // 256)
+        return 0 if tiles >= 256 else max(1, min(-(-256 // tiles), K // 512))
+
     for T in (1, 100, 2048, 8192, 32768):
-        fwd = up(T * 2 * F * 2) + up(T * F * 2)
-        assert _ws(L, D, F, T, B.PASS_FWD) == (B.UPIPE_OK, fwd)
-        assert _ws(L, D, F, T, B.PASS_BWD) == (B.UPIPE_OK, fwd + 12 * D * F)
+        base = up(T * 2 * F * 2) + up(T * F * 2)
+        sf, sb = slices(T, F), slices(T, 2 * F)
+        fwd = base + (up(sf * T * D * 4) if sf > 1 else 0)
+        bwd = base + (up(sb * T * D * 4) if sb > 1 else 0) + 12 * D * F
+        assert _ws(L, D, F, T, B.PASS_FWD) == (B.UPIPE_OK, fwd), T
+        assert _ws(L, D, F, T, B.PASS_BWD) == (B.UPIPE_OK, bwd), T
     assert _ws(1000, D, F, 5000, B.PASS_FWD) == _ws(1000, D, F, 1000, B.PASS_FWD)
     # the whole-sequence intermediates a tile avoids: at L 32768, tile 8192
     # keeps a quarter of them
