@@ -41,6 +41,8 @@ EXPORTS = (
     "upipe_profile_read",
     "upipe_pipeline_enable",
     "upipe_debug_enable",
+    "upipe_last_hip_error",
+    "upipe_last_hip_error_string",
     "upipe_strerror",
     "upipe_version",
 )
@@ -52,14 +54,25 @@ KERNEL_KINDS = {"attn_fwd": 0, "attn_bwd_dkdv": 1, "attn_bwd_dq": 2, "gemm": 3, 
 class UpipeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: status {status}: {strerror(status)}")
+        msg = f"{where}: status {status}: {strerror(status)}"
+        if status == UPIPE_EHIP:
+            self.hip_error = lib().upipe_last_hip_error()
+            msg += f" (HIP error {self.hip_error}: {lib().upipe_last_hip_error_string().decode()})"
+        super().__init__(msg)
 
 
 _lib = None
 
 
 def lib() -> ctypes.CDLL:
-    """Load the in-tree HIP library (raises if it was not built)."""
+    """Load the in-tree HIP library (raises if it was not built).
+
+    torch is imported first.  A process holds one HIP runtime per soname:
+    torch ships its own libamdhip64.so.7, and the library, linked against
+    the system ROCm's, must bind to that same copy.  Loaded the other way
+    round, the system copy comes up next to torch's as a second runtime that
+    may not see the GPU (measured: "no ROCm-capable device", while torch's
+    copy works), and every launch of the library fails."""
     global _lib
     if _lib is not None:
         return _lib
@@ -67,6 +80,8 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m headwise_chunked_context_amd.build`"
         )
+    import torch  # noqa: F401  (its HIP runtime first; see above)
+
     L = ctypes.CDLL(LIB_PATH)
     i64, i32, f64, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
     vp = ctypes.c_void_p
@@ -100,6 +115,10 @@ def lib() -> ctypes.CDLL:
     L.upipe_pipeline_enable.restype = ctypes.c_int
     L.upipe_debug_enable.argtypes = [ctypes.c_int]
     L.upipe_debug_enable.restype = ctypes.c_int
+    L.upipe_last_hip_error.argtypes = []
+    L.upipe_last_hip_error.restype = ctypes.c_int
+    L.upipe_last_hip_error_string.argtypes = []
+    L.upipe_last_hip_error_string.restype = ctypes.c_char_p
     _lib = L
     return L
 

@@ -22,6 +22,9 @@ using namespace upipe;
 
 namespace upipe {
 bool g_debug_fill = false;
+
+thread_local hipError_t t_last_hip_error = hipSuccess;
+void note_hip_error(hipError_t e) { t_last_hip_error = e; }
 }
 
 namespace {
@@ -179,9 +182,13 @@ int check_common(const Shape& s, double theta, const void* x, const void* w_qkv,
   return UPIPE_OK;
 }
 
-#define UPIPE_TRY(expr)                   \
-  do {                                    \
-    if ((expr) != hipSuccess) return UPIPE_EHIP; \
+#define UPIPE_TRY(expr)                     \
+  do {                                      \
+    const hipError_t upipe_e_ = (expr);     \
+    if (upipe_e_ != hipSuccess) {           \
+      note_hip_error(upipe_e_);             \
+      return UPIPE_EHIP;                    \
+    }                                       \
   } while (0)
 
 // ---- optional per-kernel-class timing (see upipe_profile_enable)
@@ -256,7 +263,11 @@ hipError_t debug_fill(void* p, size_t bytes, hipStream_t st) {
 
 int side_stream(Side** out) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return UPIPE_EHIP;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    note_hip_error(ge != hipSuccess ? ge : hipErrorInvalidDevice);
+    return UPIPE_EHIP;
+  }
   std::lock_guard<std::mutex> lock(g_side_mu);
   Side& sd = g_side[dev];
   if (!sd.stream) {
@@ -265,14 +276,15 @@ int side_stream(Side** out) {
     Side fresh;
     hipEvent_t* evs[5] = {&fresh.fork, &fresh.ready[0], &fresh.ready[1], &fresh.done[0],
                           &fresh.done[1]};
-    bool ok = true;
+    hipError_t err = hipSuccess;
     for (hipEvent_t* e : evs)
-      ok = ok && hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipStreamCreateWithFlags(&fresh.stream, hipStreamNonBlocking) == hipSuccess;
-    if (!ok) {
+      if (err == hipSuccess) err = hipEventCreateWithFlags(e, hipEventDisableTiming);
+    if (err == hipSuccess) err = hipStreamCreateWithFlags(&fresh.stream, hipStreamNonBlocking);
+    if (err != hipSuccess) {
       for (hipEvent_t* e : evs)
         if (*e) (void)hipEventDestroy(*e);
       if (fresh.stream) (void)hipStreamDestroy(fresh.stream);
+      note_hip_error(err);
       return UPIPE_EHIP;
     }
     sd = fresh;
@@ -355,6 +367,12 @@ int upipe_pipeline_enable(int on) {
   return UPIPE_OK;
 }
 
+int upipe_last_hip_error(void) { return (int)t_last_hip_error; }
+
+const char* upipe_last_hip_error_string(void) {
+  return t_last_hip_error == hipSuccess ? "no HIP error recorded" : hipGetErrorString(t_last_hip_error);
+}
+
 int upipe_debug_enable(int on) {
   g_debug_fill = on != 0;
   return UPIPE_OK;
@@ -377,9 +395,9 @@ int upipe_profile_read(int kind, double* total_ms, int64_t* launches) {
   if (kind < 0 || kind >= kKinds || !total_ms || !launches) return UPIPE_EINVAL;
   double sum = 0.0;
   for (auto& pr : g_prof.rec[kind]) {
-    if (hipEventSynchronize(pr.second) != hipSuccess) return UPIPE_EHIP;
+    UPIPE_TRY(hipEventSynchronize(pr.second));
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return UPIPE_EHIP;
+    UPIPE_TRY(hipEventElapsedTime(&ms, pr.first, pr.second));
     sum += ms;
   }
   *total_ms = sum;
@@ -559,11 +577,13 @@ std::mutex g_scratch_mu;
 
 int scratch_ptr(void** out) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return UPIPE_EHIP;
+  UPIPE_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return UPIPE_EUNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return UPIPE_EHIP;
+    UPIPE_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) UPIPE_TRY(hipErrorInvalidSymbol);
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
@@ -934,10 +954,10 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     const int sl = c & 1;
     if (ch.kv_first) kslot ^= 1;
     kslot_of[sl] = kslot;
-    if (c >= 2 && hipStreamWaitEvent(sb, side->done[sl], 0) != hipSuccess) return UPIPE_EHIP;
+    if (c >= 2) UPIPE_TRY(hipStreamWaitEvent(sb, side->done[sl], 0));
     const int r = stage_prepare(c, sl, kslot, sb);
     if (r != UPIPE_OK) return r;
-    if (hipEventRecord(side->ready[sl], sb) != hipSuccess) return UPIPE_EHIP;
+    UPIPE_TRY(hipEventRecord(side->ready[sl], sb));
     return UPIPE_OK;
   };
   rc = prepare(0);

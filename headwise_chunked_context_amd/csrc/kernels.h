@@ -70,6 +70,10 @@ struct GemmArgs {
 
 hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, hipStream_t s);
 
+// The HIP error behind the most recent UPIPE_EHIP of the calling thread,
+// kept for upipe_last_hip_error (hipSuccess when none)
+void note_hip_error(hipError_t e);
+
 // bf16 dst rows = the sum of nslices fp32 [M][N] slices, in slice order
 // (the partial results of a GEMM whose splits store into their own slices)
 hipError_t launch_sum_slices(const float* slices, int nslices, int M, int N, uint16_t* dst,

@@ -188,9 +188,13 @@ int check_ws(const MlpShape& s, int pass, void* ws, size_t ws_bytes) {
   return UPIPE_OK;
 }
 
-#define UPIPE_TRY(expr)                            \
-  do {                                             \
-    if ((expr) != hipSuccess) return UPIPE_EHIP;   \
+#define UPIPE_TRY(expr)                     \
+  do {                                      \
+    const hipError_t upipe_e_ = (expr);     \
+    if (upipe_e_ != hipSuccess) {           \
+      note_hip_error(upipe_e_);             \
+      return UPIPE_EHIP;                    \
+    }                                       \
   } while (0)
 
 GemmArgs gemm_args(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C,

@@ -291,6 +291,14 @@ int upipe_pipeline_enable(int on);
  */
 int upipe_debug_enable(int on);
 
+/*
+ * The HIP error behind the calling thread's most recent UPIPE_EHIP (as an
+ * int hipError_t value, 0 if none was recorded) and its HIP description
+ * (static text, never NULL).  Host-side state only.
+ */
+int upipe_last_hip_error(void);
+const char* upipe_last_hip_error_string(void);
+
 /* Static, human-readable text for a status code.  Never NULL. */
 const char* upipe_strerror(int status);
 

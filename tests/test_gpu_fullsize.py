@@ -32,12 +32,17 @@ def _gpu(w, inp, hc):
 
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+    label = f"{w.name} chunk {hc}"
+    print(f"[{label}] inputs to the GPU", flush=True)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     x, wq, wo, dy = (to_dev(inp[k]) for k in ("x", "w_qkv", "w_o", "dy"))
+    print(f"[{label}] upipe_attn_fwd", flush=True)
     y, o, lse = lib.attn_fwd(x, wq, wo, w.n_q, w.n_kv, hc, w.theta)
+    print(f"[{label}] upipe_attn_bwd", flush=True)
     dx, dwq, dwo = lib.attn_bwd(x, wq, wo, o, lse, dy, w.n_q, w.n_kv, hc, w.theta)
     torch.cuda.synchronize()
+    print(f"[{label}] done; copying results back", flush=True)
     peak = torch.cuda.max_memory_allocated()
     out = dict(o=from_dev_bf16_f32(o), lse=from_dev_f32(lse), dx=from_dev_bf16_f32(dx), peak=peak)
     if y is not None:
