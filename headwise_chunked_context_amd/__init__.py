@@ -32,6 +32,7 @@ from .binding import (  # noqa: F401
     mlp_fwd,
     mlp_workspace_bytes,
     pipeline_enable,
+    pipeline_enabled,
     profile_enable,
     profile_read,
     strerror,

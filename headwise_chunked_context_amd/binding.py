@@ -156,6 +156,11 @@ def debug_enable(on: bool) -> None:
         raise UpipeError(rc, "upipe_debug_enable")
 
 
+def pipeline_enabled() -> bool:
+    """Whether two-slot pipelining is on (as set through pipeline_enable)."""
+    return _pipeline
+
+
 def fwd_pass() -> int:
     """Workspace pass of upipe_attn_fwd under the current pipelining setting."""
     return PASS_FWD_PIPELINED if _pipeline else PASS_FWD
