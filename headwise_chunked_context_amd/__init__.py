@@ -26,9 +26,11 @@ from .binding import (  # noqa: F401
     attn_fwd_static,
     fwd_pass,
     bwd_pass,
+    choose_chunk,
     debug_enable,
     lib,
     mlp_bwd,
+    mlp_choose_tile,
     mlp_fwd,
     mlp_workspace_bytes,
     pipeline_enable,

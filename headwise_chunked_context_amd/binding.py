@@ -34,7 +34,9 @@ EXPORTS = (
     "upipe_attn_fwd",
     "upipe_attn_fwd_static",
     "upipe_attn_bwd",
+    "upipe_attn_choose_chunk",
     "upipe_mlp_workspace_bytes",
+    "upipe_mlp_choose_tile",
     "upipe_mlp_fwd",
     "upipe_mlp_bwd",
     "upipe_profile_enable",
@@ -96,6 +98,11 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_bwd.argtypes = [i64, i32, i32, i32, i32, f64, i32,
                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.upipe_attn_bwd.restype = ctypes.c_int
+    L.upipe_attn_choose_chunk.argtypes = [i64, i32, i32, i32, i32, i32, sz, ctypes.POINTER(i32),
+                                          ctypes.POINTER(sz)]
+    L.upipe_attn_choose_chunk.restype = ctypes.c_int
+    L.upipe_mlp_choose_tile.argtypes = [i64, i32, i32, i32, sz, ctypes.POINTER(i32), ctypes.POINTER(sz)]
+    L.upipe_mlp_choose_tile.restype = ctypes.c_int
     L.upipe_mlp_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(sz)]
     L.upipe_mlp_workspace_bytes.restype = ctypes.c_int
     L.upipe_mlp_fwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -146,6 +153,17 @@ def pipeline_enable(on: bool) -> None:
     if rc != UPIPE_OK:
         raise UpipeError(rc, "upipe_pipeline_enable")
     _pipeline = bool(on)
+
+
+def choose_chunk(L: int, hidden: int, n_q: int, n_kv: int, budget_bytes: int, pass_: int,
+                 head_dim: int = 128):
+    """(head_chunk, workspace bytes): the largest chunk whose workspace fits."""
+    c, b = ctypes.c_int32(0), ctypes.c_size_t(0)
+    rc = lib().upipe_attn_choose_chunk(L, hidden, n_q, n_kv, head_dim, pass_, budget_bytes,
+                                       ctypes.byref(c), ctypes.byref(b))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_attn_choose_chunk")
+    return c.value, b.value
 
 
 def debug_enable(on: bool) -> None:
@@ -349,6 +367,16 @@ def attn_bwd(x, w_qkv, w_o, o_saved, lse, dy, n_q: int, n_kv: int, head_chunk: i
 
 
 # ---------------------------------------------------------------- SwiGLU MLP
+def mlp_choose_tile(L: int, hidden: int, ffn: int, budget_bytes: int, pass_: int):
+    """(tile_rows, workspace bytes): the longest tile whose workspace fits."""
+    t, b = ctypes.c_int32(0), ctypes.c_size_t(0)
+    rc = lib().upipe_mlp_choose_tile(L, hidden, ffn, pass_, budget_bytes, ctypes.byref(t),
+                                     ctypes.byref(b))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_mlp_choose_tile")
+    return t.value, b.value
+
+
 def mlp_workspace_bytes(L: int, hidden: int, ffn: int, tile_rows: int, pass_: int) -> int:
     out = ctypes.c_size_t(0)
     rc = lib().upipe_mlp_workspace_bytes(L, hidden, ffn, tile_rows, pass_, ctypes.byref(out))

@@ -594,6 +594,32 @@ int scratch_ptr(void** out) {
 
 extern "C" {
 
+int upipe_attn_choose_chunk(int64_t seq_len, int32_t hidden, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, int32_t pass,
+                            size_t budget_bytes, int32_t* head_chunk, size_t* bytes) {
+  if (!head_chunk || !bytes || pass < UPIPE_PASS_FWD || pass > UPIPE_PASS_BWD_PIPELINED)
+    return UPIPE_EINVAL;
+  int best = 0, first_rc = UPIPE_ECHUNK;
+  size_t best_bytes = 0;
+  for (int c = 1; c <= n_q_heads; ++c) {
+    size_t b = 0;
+    const int rc = upipe_attn_workspace_bytes(seq_len, hidden, n_q_heads, n_kv_heads, head_dim, c,
+                                              pass, &b);
+    if (rc == UPIPE_ECHUNK) continue;  // not a valid chunk for these head counts
+    if (rc != UPIPE_OK) return rc;     // the shapes themselves are refused
+    first_rc = UPIPE_OK;
+    if (b <= budget_bytes) {           // the workspace grows with the chunk: keep the largest
+      best = c;
+      best_bytes = b;
+    }
+  }
+  if (first_rc != UPIPE_OK) return first_rc;
+  if (best == 0) return UPIPE_EWORKSPACE;
+  *head_chunk = best;
+  *bytes = best_bytes;
+  return UPIPE_OK;
+}
+
 int upipe_attn_fwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n_kv_heads,
                    int32_t head_dim, double rope_theta, int32_t head_chunk, const uint16_t* x,
                    const uint16_t* w_qkv, const uint16_t* w_o, uint16_t* y, uint16_t* o_saved,

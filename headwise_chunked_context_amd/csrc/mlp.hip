@@ -273,6 +273,33 @@ int upipe_mlp_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t ffn, int3
   return UPIPE_OK;
 }
 
+int upipe_mlp_choose_tile(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t pass,
+                          size_t budget_bytes, int32_t* tile_rows, size_t* bytes) {
+  if (!tile_rows || !bytes || (pass != UPIPE_PASS_FWD && pass != UPIPE_PASS_BWD)) return UPIPE_EINVAL;
+  MlpShape s;
+  int rc = check_mlp_shape(seq_len, hidden, ffn, 1, &s);
+  if (rc != UPIPE_OK) return rc;
+  // candidates: multiples of 256 rows and the whole sequence; fewer, longer
+  // tiles run faster, so the largest that fits wins (the size is not
+  // monotone in the tile where the split buffers of short tiles appear)
+  int64_t best = 0;
+  size_t best_bytes = 0;
+  for (int64_t t = 256; t < seq_len + 256; t += 256) {
+    const int64_t tt = t < seq_len ? t : seq_len;
+    MlpShape c;
+    if (check_mlp_shape(seq_len, hidden, ffn, (int32_t)tt, &c) != UPIPE_OK) continue;
+    const size_t b = make_mlp_plan(c, pass).total;
+    if (b <= budget_bytes && tt > best) {
+      best = tt;
+      best_bytes = b;
+    }
+  }
+  if (best == 0) return UPIPE_EWORKSPACE;
+  *tile_rows = (int32_t)best;
+  *bytes = best_bytes;
+  return UPIPE_OK;
+}
+
 int upipe_mlp_fwd(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t tile_rows,
                   const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
                   uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {

@@ -124,6 +124,20 @@ int upipe_attn_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t n_q_head
                                int32_t pass, size_t* bytes);
 
 /*
+ * Chunk choice for a memory budget: writes to *head_chunk the largest valid
+ * head chunk (it divides n_q_heads and keeps KV groups whole) whose
+ * workspace for `pass` is at most budget_bytes, and that workspace to
+ * *bytes.  Larger chunks run faster and need more memory, so the training
+ * run picks the chunk that fits its budget (chunk-size ablation paragraph
+ * of "Untied Ulysses Pushes Llama-3-8B Training to 5 Million Tokens").
+ * Returns UPIPE_EWORKSPACE when no chunk fits, otherwise as
+ * upipe_attn_workspace_bytes.  Host only.
+ */
+int upipe_attn_choose_chunk(int64_t seq_len, int32_t hidden, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, int32_t pass,
+                            size_t budget_bytes, int32_t* head_chunk, size_t* bytes);
+
+/*
  * Forward pass: for each head chunk in turn, project the chunk's q (k and v
  * when the chunk opens a KV group), rotate, run causal attention and store
  * the chunk's per-head output; then y = o_saved W_o^T.  The head-at-a-time

@@ -38,9 +38,14 @@
  *    hidden * ffn < 2^33, tile_rows >= 1 (a tile larger than L is L).
  *  - Precision: bf16 operands with fp32 accumulation; h, u, a, da, dh, du
  *    are held in bf16 between the GEMMs; the activation runs in fp32.
- *  - The weight gradients are reduced over the sequence by fp32 atomic
- *    adds, whose order varies from run to run: they are not bitwise
- *    reproducible.  y and dx are.
+ *  - y and dx are bitwise reproducible from run to run.  Across tile sizes
+ *    they are bit for bit equal whenever the hidden-wide GEMMs split their
+ *    reduction the same number of times (not at all once a tile gives them
+ *    256 output tiles of 256 x 256; short tiles split into fp32 slices
+ *    summed in a fixed order).  The weight gradients accumulate
+ *    over tiles in fp32, tile by tile in order; a tile whose weight-
+ *    gradient GEMM splits its reduction (short tiles of wide layers) adds
+ *    its parts by fp32 atomics, whose order can vary from run to run.
  */
 #ifndef UPIPE_MLP_H
 #define UPIPE_MLP_H
@@ -56,14 +61,26 @@ extern "C" {
 
 /*
  * Workspace size query for upipe_mlp_fwd (pass = UPIPE_PASS_FWD) or
- * upipe_mlp_bwd (pass = UPIPE_PASS_BWD).  The size is affine in tile_rows
- * (one tile's [tile, 2 ffn] and [tile, ffn] bf16 intermediates) plus, for
- * the backward, the fp32 weight-gradient accumulators (4 * 3 * hidden * ffn
- * bytes).  Returns UPIPE_OK or the error the entry point would return for
- * these shapes.  Host only.
+ * upipe_mlp_bwd (pass = UPIPE_PASS_BWD): one tile's [tile, 2 ffn] and
+ * [tile, ffn] bf16 intermediates; for tiles too short to give the hidden-
+ * wide GEMMs 256 output tiles of 256 x 256, s fp32 [tile, hidden] slices of
+ * their split reduction (s = min(ceil(256 / output tiles), K / 512), K = ffn
+ * forward and 2 ffn backward); and, for the backward, the fp32
+ * weight-gradient accumulators (4 * 3 * hidden * ffn bytes).  Returns
+ * UPIPE_OK or the error the entry point would return for these shapes.
+ * Host only.
  */
 int upipe_mlp_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t tile_rows,
                               int32_t pass, size_t* bytes);
+
+/*
+ * Tile choice for a memory budget: writes to *tile_rows the longest tile
+ * (a multiple of 256 rows, or the whole sequence) whose workspace for
+ * `pass` is at most budget_bytes, and that workspace to *bytes.  Longer
+ * tiles run faster.  Returns UPIPE_EWORKSPACE when no tile fits.  Host only.
+ */
+int upipe_mlp_choose_tile(int64_t seq_len, int32_t hidden, int32_t ffn, int32_t pass,
+                          size_t budget_bytes, int32_t* tile_rows, size_t* bytes);
 
 /*
  * Forward: y = (silu(x W_gate^T) * (x W_up^T)) W_down^T, tile by tile.

@@ -370,3 +370,24 @@ def test_debug_mode_switch_is_host_only():
     L = B.lib()
     assert L.upipe_debug_enable(1) == B.UPIPE_OK
     assert L.upipe_debug_enable(0) == B.UPIPE_OK
+
+
+@pytest.mark.parametrize("shape", [(262144, 5120, 8, 1), (32768, 4096, 32, 8), (524288, 0, 4, 1)])
+def test_choose_chunk_takes_the_largest_chunk_that_fits(shape):
+    """The chunk that fits a memory budget (chunk-size ablation paragraph):
+    the largest valid chunk whose workspace is within the budget."""
+    L, D, nq, nkv = shape
+    G = nq // nkv
+    valid = [c for c in range(1, nq + 1) if nq % c == 0 and (c % G == 0 or G % c == 0)]
+    sizes = {c: _ws(L, D, nq, nkv, 128, c, B.PASS_BWD)[1] for c in valid}
+    for c in valid:
+        got = hc_amd.choose_chunk(L, D, nq, nkv, sizes[c], B.PASS_BWD)
+        assert got == (c, sizes[c])
+        if c > 1:
+            assert hc_amd.choose_chunk(L, D, nq, nkv, sizes[c] - 1, B.PASS_BWD)[0] < c
+    with pytest.raises(B.UpipeError) as e:
+        hc_amd.choose_chunk(L, D, nq, nkv, sizes[valid[0]] - 1, B.PASS_BWD)
+    assert e.value.status == B.UPIPE_EWORKSPACE
+    with pytest.raises(B.UpipeError) as e:
+        hc_amd.choose_chunk(L, D, nq, nkv, 1 << 40, 7)
+    assert e.value.status == B.UPIPE_EINVAL

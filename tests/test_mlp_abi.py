@@ -118,3 +118,17 @@ def test_binding_checks_shapes_before_the_library():
         hc_amd.mlp_fwd(x, wgu, wd, 4)                 # host tensors
     with pytest.raises(ValueError):
         hc_amd.mlp_fwd(x, wgu[:-1], wd, 4)            # gate/up rows != 2 ffn
+
+
+def test_choose_tile_takes_the_longest_tile_that_fits():
+    L, D, F = 32768, 4096, 14336
+    for budget in (100 << 20, 500 << 20, 2 << 30, 64 << 30):
+        t, b = hc_amd.mlp_choose_tile(L, D, F, budget, B.PASS_BWD if budget > (2 << 30) else B.PASS_FWD)
+        pss = B.PASS_BWD if budget > (2 << 30) else B.PASS_FWD
+        assert b <= budget and _ws(L, D, F, t, pss) == (B.UPIPE_OK, b)
+        assert t % 256 == 0 or t == L
+        # no longer candidate fits
+        for t2 in range(t + 256, L + 256, 256):
+            assert _ws(L, D, F, min(t2, L), pss)[1] > budget
+    with pytest.raises(B.UpipeError):
+        hc_amd.mlp_choose_tile(L, D, F, 1 << 20, B.PASS_FWD)       # nothing fits
