@@ -1,5 +1,5 @@
 """fp64 CPU oracle for headwise-chunked causal GQA attention and the
-sequence-tiled SwiGLU MLP.
+sequence-tiled SwiGLU MLP and language-model loss.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this package: only the tests, the smoke check of __graft_entry__ and the
@@ -18,3 +18,4 @@ from .attention import (  # noqa: F401
     rope_angles,
 )
 from .mlp import mlp_bwd, mlp_fwd, silu, silu_grad  # noqa: F401
+from .loss import logsumexp_rows, loss_bwd, loss_fwd  # noqa: F401

@@ -18,7 +18,7 @@ import dataclasses
 
 import numpy as np
 
-TENSOR_IDS = {"x": 1, "w_qkv": 2, "w_o": 3, "dy": 4}
+TENSOR_IDS = {"x": 1, "w_qkv": 2, "w_o": 3, "dy": 4, "targets": 5}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -98,6 +98,53 @@ def make_mlp_inputs(w: MlpWorkload, with_grad: bool = True, seed_base: int | Non
     if with_grad:
         out["dy"] = draw_bf16(base + TENSOR_IDS["dy"], (w.L, w.hidden), 1.0)
     return out
+
+
+@dataclasses.dataclass(frozen=True)
+class LossWorkload:
+    """A sequence-tiled language-model loss: L positions of width hidden
+    projected onto a vocabulary of `vocab` tokens, tile_rows positions at a
+    time; one position in `ignore_every` has the ignore index as target."""
+
+    wid: int
+    name: str
+    L: int
+    hidden: int
+    vocab: int
+    tile_rows: int
+    ignore_every: int = 16
+    h_sigma: float = 1.0
+    w_sigma: float = 0.02
+
+    def with_(self, **kw) -> "LossWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+IGNORE_INDEX = -100
+
+# The Llama-3-8B output projection (hidden 4096, vocabulary 128256) over the
+# benchmarked layer's sequence, and a small one for parity tests.
+LOSS_WORKLOADS = {
+    21: LossWorkload(21, "loss_hidden256_vocab1024_L1000_tile256", 1000, 256, 1024, 256),
+    22: LossWorkload(22, "llama3_8b_loss_hidden4096_vocab128256_L32768_tile4096", 32768, 4096, 128256, 4096),
+}
+
+
+def make_loss_inputs(w: LossWorkload, seed_base: int | None = None) -> dict:
+    """h [L, hidden] and w [vocab, hidden] as bf16 bits (uint16), targets [L]
+    int32 uniform over the vocabulary with every `ignore_every`-th position
+    (from a seeded random offset) set to IGNORE_INDEX.  Seeds as for the
+    attention workloads (1000 * wid + tensor id)."""
+    base = 1000 * w.wid if seed_base is None else seed_base
+    rng = np.random.Generator(np.random.PCG64(base + TENSOR_IDS["targets"]))
+    targets = rng.integers(0, w.vocab, size=w.L, dtype=np.int64).astype(np.int32)
+    if w.ignore_every > 0:
+        targets[int(rng.integers(0, w.ignore_every))::w.ignore_every] = IGNORE_INDEX
+    return {
+        "h": draw_bf16(base + TENSOR_IDS["x"], (w.L, w.hidden), w.h_sigma),
+        "w": draw_bf16(base + TENSOR_IDS["w_qkv"], (w.vocab, w.hidden), w.w_sigma),
+        "targets": targets,
+    }
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
