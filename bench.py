@@ -42,6 +42,10 @@ preparation and the dx accumulate (an epilogue of the dx GEMMs).
 mlp_workloads: the sequence-tiled SwiGLU MLP of the same training stack at
 the Llama-3-8B shape (hidden 4096, intermediate 14336) over L 32768, forward
 + backward at tiles of 2048, 8192 and 32768 rows.
+
+loss_workloads: the sequence-tiled cross-entropy loss of the same stack at
+the Llama-3-8B output projection (hidden 4096, vocabulary 128256) over
+L 32768, forward + backward at tiles of 2048, 4096 and 8192 rows.
 """
 from __future__ import annotations
 
@@ -425,6 +429,64 @@ def mlp_sweep(lib) -> dict:
     return out
 
 
+def loss_sweep(lib) -> dict:
+    """The sequence-tiled cross-entropy loss at the Llama-3-8B output
+    projection (hidden 4096, vocabulary 128256) over L 32768, forward +
+    backward, at several tile sizes: ms per step, TFLOP/s of model work
+    (6 L hidden vocab: forward 2, backward 4; the backward's recompute of
+    the logits, 2 more, is executed, not counted), workspace and allocator
+    peak."""
+    import torch
+
+    import synthetic
+
+    base = synthetic.LOSS_WORKLOADS[22]
+    out = {}
+    g = torch.Generator(device="cuda:0").manual_seed(1000 * base.wid)
+    L, D, V = base.L, base.hidden, base.vocab
+    h = torch.randn(L, D, generator=g, device="cuda:0", dtype=torch.float32).to(torch.bfloat16)
+    w = (torch.randn(V, D, generator=g, device="cuda:0", dtype=torch.float32) * base.w_sigma).to(
+        torch.bfloat16)
+    t = torch.randint(0, V, (L,), generator=g, device="cuda:0", dtype=torch.int32)
+    t[::base.ignore_every] = synthetic.IGNORE_INDEX
+    io = sum(x.numel() * x.element_size() for x in (h, w, t))
+    for tile in (2048, 4096, 8192):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        ws_f = lib.loss_workspace_bytes(L, D, V, tile, lib.PASS_FWD)
+        ws_b = lib.loss_workspace_bytes(L, D, V, tile, lib.PASS_BWD)
+        ws = torch.empty(max(ws_f, ws_b), dtype=torch.uint8, device="cuda:0")
+
+        def step():
+            _, lse = lib.loss_fwd(h, w, t, tile, synthetic.IGNORE_INDEX, workspace=ws)
+            lib.loss_bwd(h, w, t, lse, 1.0, tile, synthetic.IGNORE_INDEX, workspace=ws)
+
+        step()
+        torch.cuda.synchronize()
+        steps = 3
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        peak = torch.cuda.max_memory_allocated()
+        del ws
+        key = f"llama3_8b_loss_hidden4096_vocab128256_L32768_tile{tile}"
+        out[key] = {
+            "seq_len": L, "hidden": D, "vocab": V, "tile_rows": tile, "steps": steps, "warmup": 1,
+            "ms_per_step": round(ms, 3),
+            "tflops": round(6.0 * L * D * V / (ms * 1e-3) / 1e12, 2),
+            "workspace_gib": {"fwd": round(ws_f / 2**30, 4), "bwd": round(ws_b / 2**30, 4)},
+            "peak_allocated_gib": round(peak / 2**30, 3),
+            "peak_allocated_minus_inputs_gib": round((peak - io) / 2**30, 3),
+            "full_sequence_fp32_logits_gib": round(L * V * 4 / 2**30, 3),
+        }
+        print(f"bench: {key}: {out[key]['ms_per_step']} ms/step, {out[key]['tflops']} TFLOP/s",
+              file=sys.stderr, flush=True)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -562,6 +624,7 @@ def main() -> int:
         del x, wq, wo, dy
         out["workloads"] = sweep(lib)
         out["mlp_workloads"] = mlp_sweep(lib)
+        out["loss_workloads"] = loss_sweep(lib)
     if not args.no_cpu_baseline and not args.seq_len:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -1,8 +1,10 @@
 """Headwise-chunked causal GQA attention (UPipe) for MI355X / gfx950, with the
-sequence-tiled SwiGLU MLP of the same long-context training stack.
+sequence-tiled SwiGLU MLP and language-model loss of the same long-context
+training stack.
 
-Both run in the HIP library libupipe_attn.so (C ABI in include/upipe_attn.h
-and include/upipe_mlp.h); this package is its thin ctypes binding.
+All run in the HIP library libupipe_attn.so (C ABI in include/upipe_attn.h,
+include/upipe_mlp.h and include/upipe_loss.h); this package is its thin
+ctypes binding.
 """
 from .binding import (  # noqa: F401
     EXPORTS,
@@ -29,6 +31,10 @@ from .binding import (  # noqa: F401
     choose_chunk,
     debug_enable,
     lib,
+    loss_bwd,
+    loss_choose_tile,
+    loss_fwd,
+    loss_workspace_bytes,
     mlp_bwd,
     mlp_choose_tile,
     mlp_fwd,

@@ -28,7 +28,8 @@ PASS_FWD_PIPELINED = 3
 PASS_BWD_PIPELINED = 4
 _pipeline = False
 
-# names declared in include/upipe_attn.h and include/upipe_mlp.h
+# names declared in include/upipe_attn.h, include/upipe_mlp.h and
+# include/upipe_loss.h
 EXPORTS = (
     "upipe_attn_workspace_bytes",
     "upipe_attn_fwd",
@@ -39,6 +40,10 @@ EXPORTS = (
     "upipe_mlp_choose_tile",
     "upipe_mlp_fwd",
     "upipe_mlp_bwd",
+    "upipe_loss_workspace_bytes",
+    "upipe_loss_choose_tile",
+    "upipe_loss_fwd",
+    "upipe_loss_bwd",
     "upipe_profile_enable",
     "upipe_profile_read",
     "upipe_pipeline_enable",
@@ -109,6 +114,15 @@ def lib() -> ctypes.CDLL:
     L.upipe_mlp_fwd.restype = ctypes.c_int
     L.upipe_mlp_bwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.upipe_mlp_bwd.restype = ctypes.c_int
+    L.upipe_loss_choose_tile.argtypes = [i64, i32, i32, i32, sz, ctypes.POINTER(i32), ctypes.POINTER(sz)]
+    L.upipe_loss_choose_tile.restype = ctypes.c_int
+    L.upipe_loss_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.upipe_loss_workspace_bytes.restype = ctypes.c_int
+    L.upipe_loss_fwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    L.upipe_loss_fwd.restype = ctypes.c_int
+    L.upipe_loss_bwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp,
+                                 vp, sz, vp]
+    L.upipe_loss_bwd.restype = ctypes.c_int
     L.upipe_strerror.argtypes = [ctypes.c_int]
     L.upipe_strerror.restype = ctypes.c_char_p
     L.upipe_version.argtypes = []
@@ -432,3 +446,73 @@ def mlp_bwd(x, w_gate_up, w_down, dy, tile_rows: int, workspace=None, stream=Non
     if rc != UPIPE_OK:
         raise UpipeError(rc, "upipe_mlp_bwd")
     return dx, dwgu, dwd
+
+
+# ---------------------------------------------------------------- tiled loss
+def loss_choose_tile(L: int, hidden: int, vocab: int, budget_bytes: int, pass_: int):
+    """(tile_rows, workspace bytes): the longest tile whose workspace fits."""
+    t, b = ctypes.c_int32(0), ctypes.c_size_t(0)
+    rc = lib().upipe_loss_choose_tile(L, hidden, vocab, pass_, budget_bytes, ctypes.byref(t),
+                                      ctypes.byref(b))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_loss_choose_tile")
+    return t.value, b.value
+
+
+def loss_workspace_bytes(L: int, hidden: int, vocab: int, tile_rows: int, pass_: int) -> int:
+    out = ctypes.c_size_t(0)
+    rc = lib().upipe_loss_workspace_bytes(L, hidden, vocab, tile_rows, pass_, ctypes.byref(out))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_loss_workspace_bytes")
+    return out.value
+
+
+def _check_loss(h, w, targets):
+    import torch
+
+    if h is None or h.dim() != 2:
+        raise ValueError("h must be a 2-D tensor")
+    L, hidden = h.shape
+    if w is None or w.dim() != 2:
+        raise ValueError("w must be a 2-D tensor")
+    vocab = w.shape[0]
+    _check(h, "h", (L, hidden), torch.bfloat16)
+    _check(w, "w", (vocab, hidden), torch.bfloat16, h.device)
+    _check(targets, "targets", (L,), torch.int32, h.device)
+    return L, hidden, vocab
+
+
+def loss_fwd(h, w, targets, tile_rows: int, ignore_index: int = -100, workspace=None, stream=None):
+    """Sequence-tiled mean cross-entropy of logits = h w^T against targets
+    (rows with ignore_index do not count).  Returns (loss [1] fp32, lse [L]
+    fp32)."""
+    import torch
+
+    L, hidden, vocab = _check_loss(h, w, targets)
+    loss = torch.empty(1, dtype=torch.float32, device=h.device)
+    lse = torch.empty(L, dtype=torch.float32, device=h.device)
+    ws = _workspace(loss_workspace_bytes(L, hidden, vocab, tile_rows, PASS_FWD), h.device, workspace)
+    rc = lib().upipe_loss_fwd(L, hidden, vocab, tile_rows, _ptr(h), _ptr(w), _ptr(targets),
+                              ignore_index, _ptr(loss), _ptr(lse), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_loss_fwd")
+    return loss, lse
+
+
+def loss_bwd(h, w, targets, lse, dloss: float, tile_rows: int, ignore_index: int = -100,
+             workspace=None, stream=None):
+    """Backward of loss_fwd with upstream gradient dloss.  Returns (dh, dw)."""
+    import torch
+
+    L, hidden, vocab = _check_loss(h, w, targets)
+    _check(lse, "lse", (L,), torch.float32, h.device)
+    dh = torch.empty_like(h)
+    dw = torch.empty_like(w)
+    ws = _workspace(loss_workspace_bytes(L, hidden, vocab, tile_rows, PASS_BWD), h.device, workspace)
+    rc = lib().upipe_loss_bwd(L, hidden, vocab, tile_rows, _ptr(h), _ptr(w), _ptr(targets),
+                              ignore_index, _ptr(lse), float(dloss), _ptr(dh), _ptr(dw), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_loss_bwd")
+    return dh, dw

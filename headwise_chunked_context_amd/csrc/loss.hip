@@ -1,0 +1,440 @@
+// C ABI of the sequence-tiled language-model loss (include/upipe_loss.h):
+// argument checks, workspace planning, the tile loop, and the row kernels.
+//
+// The loss is the mean cross-entropy of next-token training over the
+// vocabulary projection of the final hidden states; computing it a tile of
+// positions at a time is the Arctic Long Sequence Training step of the
+// memory progression in "Untied Ulysses Pushes Llama-3-8B Training to 5
+// Million Tokens" (losses and MLPs need not allocate sequence-wide buffers).
+// Per tile of T rows, on the layer's bf16 MFMA GEMM (gemm.hip):
+//   forward   logits = h_t W^T                  (NT, fp32 [T, V])
+//             lse_r, loss_r per row              (ce_rows_fwd_kernel)
+//             loss = sum of loss_r / count       (ce_reduce_kernel, fixed order)
+//   backward  logits = h_t W^T                  (recomputed)
+//             dlogits = (exp(logits - lse) - onehot) * dloss / count
+//                                                (ce_rows_bwd_kernel, bf16)
+//             dh_t = dlogits W                   (NN; short tiles split the
+//                                                 vocabulary reduction into fp32
+//                                                 slices summed in order)
+//             dW += dlogits^T h_t                (TN, one split: the first tile
+//                                                 stores, later tiles add; fp32
+//                                                 accumulator the size of W)
+// Only [T, V] buffers exist, never [L, V]; the forward hands the backward
+// the per-row log-sum-exp (4 bytes per position).
+#include <math.h>
+#include <string.h>
+
+#include "../../include/upipe_loss.h"
+#include "kernels.h"
+
+using namespace upipe;
+
+namespace {
+
+constexpr int64_t kMaxL = int64_t(1) << 24;
+constexpr size_t kAlign = 256;
+constexpr int kCUs = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+// A quiet NaN built from its bits behind an empty asm: device code is built
+// with -fno-honor-nans, under which a NaN constant is undefined.
+__device__ __forceinline__ float quiet_nan() {
+  uint32_t b = 0x7fc00000u;
+  asm volatile("" : "+v"(b));
+  return __builtin_bit_cast(float, b);
+}
+
+// (m, s) summarises a set of values y (base-2 logits, y = x log2 e) as its
+// maximum m and s = sum 2^(y - m); two summaries combine exactly.
+__device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -__builtin_inff()) return;  // both empty
+  s = s * __builtin_amdgcn_exp2f(m - mm) + s2 * __builtin_amdgcn_exp2f(m2 - mm);
+  m = mm;
+}
+
+// One workgroup per row of the tile: the row's log-sum-exp (one pass over
+// the fp32 logits, online maximum) and its loss lse - logit[target] (0 for
+// an ignored row, NaN for a target outside the vocabulary).
+__global__ __launch_bounds__(256) void ce_rows_fwd_kernel(const float* logits, int V,
+                                                          const int32_t* targets, int64_t row0,
+                                                          int ignore_index, float* lse,
+                                                          float* loss_rows) {
+  __shared__ float sm_m[4], sm_s[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r = blockIdx.x;
+  const float* lg = logits + r * V;
+  float m = -__builtin_inff(), s = 0.f;
+  for (int j = tid * 4; j < V; j += 1024) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(lg + j);
+    const float y0 = x[0] * kLog2e, y1 = x[1] * kLog2e, y2 = x[2] * kLog2e, y3 = x[3] * kLog2e;
+    const float mx = fmaxf(fmaxf(y0, y1), fmaxf(y2, y3));
+    if (mx > m) {
+      s *= __builtin_amdgcn_exp2f(m - mx);
+      m = mx;
+    }
+    s += __builtin_amdgcn_exp2f(y0 - m) + __builtin_amdgcn_exp2f(y1 - m) +
+         __builtin_amdgcn_exp2f(y2 - m) + __builtin_amdgcn_exp2f(y3 - m);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+    lse_combine(m, s, m2, s2);
+  }
+  if (lane == 0) {
+    sm_m[wave] = m;
+    sm_s[wave] = s;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  m = sm_m[0];
+  s = sm_s[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) lse_combine(m, s, sm_m[w], sm_s[w]);
+  const float l = (m + __builtin_amdgcn_logf(s)) * kLn2;  // v_log_f32 is base 2
+  const int64_t row = row0 + r;
+  const int t = targets[row];
+  float loss = 0.f;
+  if (t != ignore_index) loss = (t >= 0 && t < V) ? l - lg[t] : quiet_nan();
+  lse[row] = l;
+  loss_rows[row] = loss;
+}
+
+// Rows that count (target != ignore_index), and either the mean of their
+// loss (loss != nullptr) or the backward's scale dloss / count, on one
+// workgroup: every thread sums a fixed stride of rows in fp64 and the
+// partial sums meet in a fixed order, so the result has the same bits on
+// every run.  No row counts: loss 0, scale 0.
+__global__ __launch_bounds__(1024) void ce_reduce_kernel(const float* loss_rows,
+                                                         const int32_t* targets, int64_t L,
+                                                         int ignore_index, float dloss,
+                                                         float* loss, float* scale) {
+  __shared__ double sm_sum[16];
+  __shared__ long long sm_cnt[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  double sum = 0.0;
+  long long cnt = 0;
+  for (int64_t r = tid; r < L; r += 1024) {
+    if (targets[r] == ignore_index) continue;
+    ++cnt;
+    if (loss) sum += (double)loss_rows[r];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    sum += __shfl_xor(sum, off);
+    cnt += __shfl_xor(cnt, off);
+  }
+  if (lane == 0) {
+    sm_sum[wave] = sum;
+    sm_cnt[wave] = cnt;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  sum = 0.0;
+  cnt = 0;
+  for (int w = 0; w < 16; ++w) {
+    sum += sm_sum[w];
+    cnt += sm_cnt[w];
+  }
+  if (loss) *loss = cnt > 0 ? (float)(sum / (double)cnt) : 0.f;
+  if (scale) *scale = cnt > 0 ? (float)((double)dloss / (double)cnt) : 0.f;
+}
+
+// dlogits[r][j] = (exp(logits[r][j] - lse_r) - [j == t_r]) * scale, bf16;
+// 0 for an ignored row, NaN for a target outside the vocabulary.  One
+// thread per 8 consecutive vocabulary entries of a row.
+__global__ __launch_bounds__(256) void ce_rows_bwd_kernel(const float* logits, int V,
+                                                          const int32_t* targets, int64_t row0,
+                                                          int rows, const float* lse,
+                                                          const float* scale, int ignore_index,
+                                                          uint16_t* dlogits) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = V / 8;
+  if (idx >= (int64_t)rows * cpr) return;
+  const int64_t r = idx / cpr;
+  const int j = (int)(idx % cpr) * 8;
+  const int64_t row = row0 + r;
+  const int t = targets[row];
+  const float sc = *scale;
+  float p[8];
+  if (t == ignore_index) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = 0.f;
+  } else {
+    const float l2 = lse[row] * kLog2e;
+    const float* lg = logits + r * V + j;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(lg);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(lg + 4);
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const bool in_range = t >= 0 && t < V;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v = __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -l2));
+      if (j + i == t) v -= 1.f;
+      p[i] = in_range ? v * sc : quiet_nan();
+    }
+  }
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+  *reinterpret_cast<u32x4*>(dlogits + r * V + j) = out;
+}
+
+struct LossShape {
+  int64_t L;
+  int D, V, T;  // T = rows per tile (at most L)
+};
+
+int check_loss_shape(int64_t L, int32_t hidden, int32_t vocab, int32_t tile_rows, LossShape* s) {
+  if (L < 1 || hidden < 1 || vocab < 1 || tile_rows < 1) return UPIPE_EINVAL;
+  if (L > kMaxL || hidden % 128 != 0 || vocab % 128 != 0) return UPIPE_EUNSUPPORTED;
+  if ((int64_t)hidden * vocab >= (int64_t(1) << 33)) return UPIPE_EUNSUPPORTED;
+  s->L = L;
+  s->D = hidden;
+  s->V = vocab;
+  s->T = (int)(tile_rows < L ? tile_rows : L);
+  // launch grids stay below 2^32 work-items: GEMMs of 256 x 256 tiles on 512
+  // threads (the dh GEMM with up to 256 splits), the gradient rows one thread
+  // per 8 entries
+  const int64_t lim = (int64_t)UINT32_MAX;
+  const int64_t mt = (s->T + 255) / 256;
+  if (mt * ((vocab + 255) / 256) * 512 > lim || mt * ((hidden + 255) / 256) * 256 * 512 > lim ||
+      ((int64_t)vocab + 255) / 256 * ((hidden + 255) / 256) * 512 > lim ||
+      (int64_t)s->T * (vocab / 8) + 255 > lim)
+    return UPIPE_EUNSUPPORTED;
+  return UPIPE_OK;
+}
+
+// splits of the dh GEMM ([T, hidden] output, reduction over the vocabulary):
+// enough 256 x 256 workgroups to fill the chip, each split at least 8 k steps
+int dh_splits(const LossShape& s) {
+  const int64_t tiles = (int64_t)((s.T + 255) / 256) * ((s.D + 255) / 256);
+  if (tiles >= kCUs) return 1;
+  int sp = (int)((kCUs + tiles - 1) / tiles);
+  const int max_sp = s.V / 512;
+  if (sp > max_sp) sp = max_sp;
+  return sp < 1 ? 1 : sp;
+}
+
+struct LossPlan {
+  size_t logits;     // [T][V] fp32
+  size_t dlogits;    // [T][V] bf16 (backward)
+  size_t loss_rows;  // [L] fp32 per-row loss (forward)
+  size_t dh_acc;     // [splits][T][D] fp32 partial dh (backward, split only)
+  size_t dw_acc;     // [V][D] fp32 dW accumulator (backward)
+  size_t scale;      // one fp32: dloss / count (backward)
+  size_t total;
+};
+
+LossPlan make_loss_plan(const LossShape& s, int pass) {
+  LossPlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t T = (size_t)s.T, D = (size_t)s.D, V = (size_t)s.V;
+  const size_t none = (size_t)-1;
+  p.logits = take(T * V * 4);
+  if (pass == UPIPE_PASS_BWD) {
+    p.dlogits = take(T * V * 2);
+    p.loss_rows = none;
+    const int sp = dh_splits(s);
+    p.dh_acc = sp > 1 ? take((size_t)sp * T * D * 4) : none;
+    p.dw_acc = take(V * D * 4);
+    p.scale = take(4);
+  } else {
+    p.dlogits = p.dh_acc = p.dw_acc = p.scale = none;
+    p.loss_rows = take((size_t)s.L * 4);
+  }
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return off == (size_t)-1 ? nullptr : reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int check_ws(const LossShape& s, int pass, void* ws, size_t ws_bytes) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0 ||
+      ws_bytes < make_loss_plan(s, pass).total)
+    return UPIPE_EWORKSPACE;
+  return UPIPE_OK;
+}
+
+#define UPIPE_TRY(expr)                     \
+  do {                                      \
+    const hipError_t upipe_e_ = (expr);     \
+    if (upipe_e_ != hipSuccess) {           \
+      note_hip_error(upipe_e_);             \
+      return UPIPE_EHIP;                    \
+    }                                       \
+  } while (0)
+
+GemmArgs gemm_args(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C,
+                   int64_t ldc, int M, int N, int K) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.ldb = ldb;
+  g.C = C;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.k_per_split = K;
+  return g;
+}
+
+// logits of one tile: fp32 [rows][V] = h_t W^T
+hipError_t launch_logits(const uint16_t* ht, const uint16_t* w, float* logits, int rows,
+                         const LossShape& s, hipStream_t st) {
+  return launch_gemm(GEMM_NT, EPI_STORE_F32, gemm_args(ht, s.D, w, s.D, logits, 0, rows, s.V, s.D),
+                     st);
+}
+
+// debug mode: the tile's buffers are NaN-filled before the tile
+hipError_t debug_fill_tile(float* logits, uint16_t* dlogits, const LossShape& s, hipStream_t st) {
+  if (!g_debug_fill) return hipSuccess;
+  hipError_t e = launch_fill(logits, (size_t)s.T * s.V * 4, 0xFFFFFFFFu, st);
+  if (e != hipSuccess || !dlogits) return e;
+  return launch_fill(dlogits, (size_t)s.T * s.V * 2, 0xFFFFFFFFu, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int upipe_loss_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_rows,
+                               int32_t pass, size_t* bytes) {
+  if (!bytes || (pass != UPIPE_PASS_FWD && pass != UPIPE_PASS_BWD)) return UPIPE_EINVAL;
+  LossShape s;
+  const int rc = check_loss_shape(seq_len, hidden, vocab, tile_rows, &s);
+  if (rc != UPIPE_OK) return rc;
+  *bytes = make_loss_plan(s, pass).total;
+  return UPIPE_OK;
+}
+
+int upipe_loss_choose_tile(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t pass,
+                           size_t budget_bytes, int32_t* tile_rows, size_t* bytes) {
+  if (!tile_rows || !bytes || (pass != UPIPE_PASS_FWD && pass != UPIPE_PASS_BWD)) return UPIPE_EINVAL;
+  LossShape s;
+  int rc = check_loss_shape(seq_len, hidden, vocab, 1, &s);
+  if (rc != UPIPE_OK) return rc;
+  // candidates: multiples of 256 rows and the whole sequence; the largest
+  // that fits wins (the size is not monotone in the tile where the split
+  // buffers of short tiles appear)
+  int64_t best = 0;
+  size_t best_bytes = 0;
+  for (int64_t t = 256; t < seq_len + 256; t += 256) {
+    const int64_t tt = t < seq_len ? t : seq_len;
+    LossShape c;
+    if (check_loss_shape(seq_len, hidden, vocab, (int32_t)tt, &c) != UPIPE_OK) continue;
+    const size_t b = make_loss_plan(c, pass).total;
+    if (b <= budget_bytes && tt > best) {
+      best = tt;
+      best_bytes = b;
+    }
+  }
+  if (best == 0) return UPIPE_EWORKSPACE;
+  *tile_rows = (int32_t)best;
+  *bytes = best_bytes;
+  return UPIPE_OK;
+}
+
+int upipe_loss_fwd(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_rows,
+                   const uint16_t* h, const uint16_t* w, const int32_t* targets,
+                   int32_t ignore_index, float* loss, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  LossShape s;
+  int rc = check_loss_shape(seq_len, hidden, vocab, tile_rows, &s);
+  if (rc != UPIPE_OK) return rc;
+  if (!h || !w || !targets || !loss || !lse) return UPIPE_EINVAL;
+  if (!aligned16(h) || !aligned16(w) || !aligned4(targets) || !aligned4(loss) || !aligned4(lse))
+    return UPIPE_EINVAL;
+  rc = check_ws(s, UPIPE_PASS_FWD, workspace, workspace_bytes);
+  if (rc != UPIPE_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const LossPlan p = make_loss_plan(s, UPIPE_PASS_FWD);
+  float* logits = at<float>(workspace, p.logits);
+  float* loss_rows = at<float>(workspace, p.loss_rows);
+  for (int64_t t0 = 0; t0 < s.L; t0 += s.T) {
+    const int rows = (int)(s.L - t0 < s.T ? s.L - t0 : s.T);
+    UPIPE_TRY(debug_fill_tile(logits, nullptr, s, st));
+    UPIPE_TRY(launch_logits(h + t0 * s.D, w, logits, rows, s, st));
+    hipLaunchKernelGGL(ce_rows_fwd_kernel, dim3((unsigned)rows), dim3(256), 0, st, logits, s.V,
+                       targets, t0, ignore_index, lse, loss_rows);
+    UPIPE_TRY(hipGetLastError());
+  }
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3(1), dim3(1024), 0, st, loss_rows, targets, s.L,
+                     ignore_index, 0.f, loss, (float*)nullptr);
+  UPIPE_TRY(hipGetLastError());
+  return UPIPE_OK;
+}
+
+int upipe_loss_bwd(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_rows,
+                   const uint16_t* h, const uint16_t* w, const int32_t* targets,
+                   int32_t ignore_index, const float* lse, float dloss, uint16_t* dh,
+                   uint16_t* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  LossShape s;
+  int rc = check_loss_shape(seq_len, hidden, vocab, tile_rows, &s);
+  if (rc != UPIPE_OK) return rc;
+  if (!h || !w || !targets || !lse || !dh || !dw) return UPIPE_EINVAL;
+  if (!aligned16(h) || !aligned16(w) || !aligned4(targets) || !aligned4(lse) || !aligned16(dh) ||
+      !aligned16(dw))
+    return UPIPE_EINVAL;
+  rc = check_ws(s, UPIPE_PASS_BWD, workspace, workspace_bytes);
+  if (rc != UPIPE_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const LossPlan p = make_loss_plan(s, UPIPE_PASS_BWD);
+  float* logits = at<float>(workspace, p.logits);
+  uint16_t* dlogits = at<uint16_t>(workspace, p.dlogits);
+  float* dh_acc = at<float>(workspace, p.dh_acc);
+  float* dw_acc = at<float>(workspace, p.dw_acc);
+  float* scale = at<float>(workspace, p.scale);
+  const int D = s.D, V = s.V;
+  const int splits = dh_acc ? dh_splits(s) : 1;
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3(1), dim3(1024), 0, st, (const float*)nullptr, targets,
+                     s.L, ignore_index, dloss, (float*)nullptr, scale);
+  UPIPE_TRY(hipGetLastError());
+  for (int64_t t0 = 0; t0 < s.L; t0 += s.T) {
+    const int rows = (int)(s.L - t0 < s.T ? s.L - t0 : s.T);
+    const uint16_t* ht = h + t0 * D;
+    UPIPE_TRY(debug_fill_tile(logits, dlogits, s, st));
+    UPIPE_TRY(launch_logits(ht, w, logits, rows, s, st));
+    const int64_t chunks = (int64_t)rows * (V / 8);
+    hipLaunchKernelGGL(ce_rows_bwd_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                       st, logits, V, targets, t0, rows, lse, scale, ignore_index, dlogits);
+    UPIPE_TRY(hipGetLastError());
+    // dh_t = dlogits W: one split stores bf16, several store fp32 slices
+    // summed in split order
+    if (splits <= 1) {
+      UPIPE_TRY(launch_gemm(GEMM_NN, EPI_STORE_BF16,
+                            gemm_args(dlogits, V, w, D, dh + t0 * D, D, rows, D, V), st));
+    } else {
+      GemmArgs g = gemm_args(dlogits, V, w, D, dh_acc, 0, rows, D, V);
+      g.k_per_split = gemm_k_per_split(V, splits);
+      const int used = (V + g.k_per_split - 1) / g.k_per_split;
+      UPIPE_TRY(launch_gemm(GEMM_NN, EPI_STORE_F32, g, st));
+      UPIPE_TRY(launch_sum_slices(dh_acc, used, rows, D, dh + t0 * D, D, st));
+    }
+    // dW += dlogits^T h_t, one split: the first tile stores, later ones add
+    // (plain stores; the tiles run in order on one stream)
+    GemmArgs g = gemm_args(dlogits, V, ht, D, dw_acc, 0, V, D, rows);
+    g.k_per_split = gemm_k_per_split(rows, 1);
+    UPIPE_TRY(launch_gemm(GEMM_TN, t0 == 0 ? EPI_STORE_F32 : EPI_ADD_F32, g, st));
+  }
+  RowSegments ident;
+  memset(&ident, 0, sizeof(ident));
+  UPIPE_TRY(launch_acc_to_bf16(dw_acc, V, D, dw, D, ident, st));
+  return UPIPE_OK;
+}
+
+}  // extern "C"
