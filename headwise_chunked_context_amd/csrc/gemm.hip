@@ -417,6 +417,65 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
       const int r = c >> 5, cc = c & 31;
       const int m = m0 + half * 128 + r;
       const int n = n0 + cc * 8;
+      if (EPI == EPI_CE_STATS) {
+        // the 32 lanes of a half-wave hold one row's 256 columns, 8 each:
+        // its maximum and sum of 2^(y - max), y = logit log2 e, over the
+        // tile's columns inside N (every lane takes part in the exchanges)
+        const float* src = Cs + r * BN + cc * 8;
+        const bool row_ok = m < p.M;
+        float y[8], mx = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          y[i] = row_ok && n + i < p.N ? src[i] * kLog2e : -__builtin_inff();
+          mx = fmaxf(mx, y[i]);
+        }
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        float sum = 0.f;
+        if (mx != -__builtin_inff()) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sum += __builtin_amdgcn_exp2f(y[i] - mx);
+        }
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+        if (row_ok) {
+          if (cc == 0) {
+            const int nct = (p.N + BN - 1) / BN;
+            *reinterpret_cast<f32x2*>(p.ce_stats + ((int64_t)m * nct + n0 / BN) * 2) = f32x2{mx, sum};
+          }
+          const int t = p.ce_targets[p.ce_row0 + m];
+          if (t >= n && t < n + 8 && t < p.N) p.ce_tlogit[m] = src[t - n];
+        }
+        continue;
+      }
+      if (EPI == EPI_CE_GRAD) {
+        // dlogits = (exp(logit - lse) - [n == target]) * scale, 0 for an
+        // ignored row, NaN for a target outside [0, N)
+        if (m < p.M && n < p.N) {
+          const float* src = Cs + r * BN + cc * 8;
+          const int64_t row = p.ce_row0 + m;
+          const int t = p.ce_targets[row];
+          float v[8];
+          if (t == p.ce_ignore) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = 0.f;
+          } else {
+            const float l2 = p.ce_lse[row] * kLog2e, sc = *p.ce_scale;
+            const bool in_range = t >= 0 && t < p.N;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              float e = __builtin_amdgcn_exp2f(fmaf(src[i], kLog2e, -l2));
+              if (n + i == t) e -= 1.f;
+              v[i] = in_range ? e * sc : quiet_nan();
+            }
+          }
+          u32x4 out;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+          *reinterpret_cast<u32x4*>(C + (int64_t)m * p.ldc + n) = out;
+        }
+        continue;
+      }
       const bool head_major = EPI == EPI_STORE_BF16 && n < p.hm_end;
       const int rows = head_major || p.rows_valid <= 0 ? p.M : p.rows_valid;
       if (m < rows && n < p.N) {
@@ -539,6 +598,8 @@ hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, h
       else if (epi == EPI_ACCUM_BF16) UPIPE_GEMM_CASE(true, true, EPI_ACCUM_BF16);
       else if (epi == EPI_ATOMIC_F32) UPIPE_GEMM_CASE(true, true, EPI_ATOMIC_F32);
       else if (epi == EPI_STORE_F32) UPIPE_GEMM_CASE(true, true, EPI_STORE_F32);
+      else if (epi == EPI_CE_STATS) UPIPE_GEMM_CASE(true, true, EPI_CE_STATS);
+      else if (epi == EPI_CE_GRAD) UPIPE_GEMM_CASE(true, true, EPI_CE_GRAD);
       else return hipErrorInvalidValue;
       break;
     case GEMM_NN:

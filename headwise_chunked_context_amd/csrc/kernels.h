@@ -22,17 +22,32 @@ struct RowSegments {
   int64_t row0[3];     // memory row of the segment's first logical row
 };
 
+// A quiet NaN built from its bits behind an empty asm: device code is built
+// with -fno-honor-nans, under which a NaN constant is undefined.
+__device__ __forceinline__ float quiet_nan() {
+  uint32_t b = 0x7fc00000u;
+  asm volatile("" : "+v"(b));
+  return __builtin_bit_cast(float, b);
+}
+
 enum GemmLayout { GEMM_NT = 0, GEMM_NN = 1, GEMM_TN = 2 };
 // EPI_STORE_F32 writes each split's fp32 partial tile into its own [M][N]
 // slice of C (slice s at C + s*M*N; one split: C itself); EPI_ADD_F32 adds
 // the fp32 tile into C with plain stores (TN, one split: each element has
-// one writer); EPI_ATOMIC_F32 adds with atomics (any split count)
+// one writer); EPI_ATOMIC_F32 adds with atomics (any split count).  The
+// cross-entropy epilogues (NT, one split) take C = logits of sequence rows
+// ce_row0 + m: EPI_CE_STATS stores no logits, only each row's maximum and
+// sum of 2^(y - max) (y = logit log2 e) over every 256-column tile, and the
+// target's logit; EPI_CE_GRAD stores bf16 (exp(logit - lse) - onehot) *
+// scale.
 enum GemmEpilogue {
   EPI_STORE_BF16 = 0,
   EPI_ACCUM_BF16 = 1,
   EPI_ATOMIC_F32 = 2,
   EPI_STORE_F32 = 3,
-  EPI_ADD_F32 = 4
+  EPI_ADD_F32 = 4,
+  EPI_CE_STATS = 5,
+  EPI_CE_GRAD = 6
 };
 
 struct GemmArgs {
@@ -65,6 +80,17 @@ struct GemmArgs {
   // last one) and rows of C that are stored; M may then exceed it, for the
   // head-major columns' padding rows
   int rows_valid;
+  // cross-entropy epilogues: targets and ignore index of the sequence rows
+  // (row m of C is row ce_row0 + m); EPI_CE_STATS writes ce_stats [M][ceil(N
+  // / 256)] (max, sum) pairs and ce_tlogit [M] (rows whose target lies in
+  // [0, N)); EPI_CE_GRAD reads ce_lse [L] (natural log) and *ce_scale
+  const int32_t* ce_targets;
+  int ce_ignore;
+  int64_t ce_row0;
+  float* ce_stats;
+  float* ce_tlogit;
+  const float* ce_lse;
+  const float* ce_scale;
   RopeTable rope;
 };
 

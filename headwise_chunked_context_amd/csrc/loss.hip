@@ -7,20 +7,23 @@
 // memory progression in "Untied Ulysses Pushes Llama-3-8B Training to 5
 // Million Tokens" (losses and MLPs need not allocate sequence-wide buffers).
 // Per tile of T rows, on the layer's bf16 MFMA GEMM (gemm.hip):
-//   forward   logits = h_t W^T                  (NT, fp32 [T, V])
-//             lse_r, loss_r per row              (ce_rows_fwd_kernel)
-//             loss = sum of loss_r / count       (ce_reduce_kernel, fixed order)
-//   backward  logits = h_t W^T                  (recomputed)
-//             dlogits = (exp(logits - lse) - onehot) * dloss / count
-//                                                (ce_rows_bwd_kernel, bf16)
-//             dh_t = dlogits W                   (NN; short tiles split the
-//                                                 vocabulary reduction into fp32
-//                                                 slices summed in order)
-//             dW += dlogits^T h_t                (TN, one split: the first tile
-//                                                 stores, later tiles add; fp32
-//                                                 accumulator the size of W)
-// Only [T, V] buffers exist, never [L, V]; the forward hands the backward
-// the per-row log-sum-exp (4 bytes per position).
+//   forward   logits = h_t W^T, kept in registers: the GEMM's epilogue
+//             (EPI_CE_STATS) reduces each row over each 256-column tile to
+//             (max, sum 2^(y - max)) and picks out the target's logit
+//             lse_r, loss_r per row from those pairs   (ce_combine_kernel)
+//             loss = sum of loss_r / count     (ce_reduce_kernel, fixed order)
+//   backward  logits = h_t W^T recomputed, and the epilogue (EPI_CE_GRAD)
+//             stores dlogits = (exp(logits - lse) - onehot) * dloss / count
+//             in bf16
+//             dh_t = dlogits W                 (NN; short tiles split the
+//                                               vocabulary reduction into fp32
+//                                               slices summed in order)
+//             dW += dlogits^T h_t              (TN, one split: the first tile
+//                                               stores, later tiles add; fp32
+//                                               accumulator the size of W)
+// No fp32 logits are ever stored: the forward keeps 8 bytes per row and
+// 256-column tile, the backward one bf16 [T, V] tile; the forward hands the
+// backward the per-row log-sum-exp (4 bytes per position).
 #include <math.h>
 #include <string.h>
 
@@ -39,14 +42,6 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 
-// A quiet NaN built from its bits behind an empty asm: device code is built
-// with -fno-honor-nans, under which a NaN constant is undefined.
-__device__ __forceinline__ float quiet_nan() {
-  uint32_t b = 0x7fc00000u;
-  asm volatile("" : "+v"(b));
-  return __builtin_bit_cast(float, b);
-}
-
 // (m, s) summarises a set of values y (base-2 logits, y = x log2 e) as its
 // maximum m and s = sum 2^(y - m); two summaries combine exactly.
 __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
@@ -56,28 +51,21 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
   m = mm;
 }
 
-// One workgroup per row of the tile: the row's log-sum-exp (one pass over
-// the fp32 logits, online maximum) and its loss lse - logit[target] (0 for
-// an ignored row, NaN for a target outside the vocabulary).
-__global__ __launch_bounds__(256) void ce_rows_fwd_kernel(const float* logits, int V,
-                                                          const int32_t* targets, int64_t row0,
-                                                          int ignore_index, float* lse,
-                                                          float* loss_rows) {
+// One workgroup per row of the tile: the row's log-sum-exp from the
+// (max, sum) pairs of its 256-column tiles, and its loss lse - logit[target]
+// (0 for an ignored row, NaN for a target outside the vocabulary).
+__global__ __launch_bounds__(256) void ce_combine_kernel(const float* stats, int nct,
+                                                         const float* tlogit, int V,
+                                                         const int32_t* targets, int64_t row0,
+                                                         int ignore_index, float* lse,
+                                                         float* loss_rows) {
   __shared__ float sm_m[4], sm_s[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t r = blockIdx.x;
-  const float* lg = logits + r * V;
   float m = -__builtin_inff(), s = 0.f;
-  for (int j = tid * 4; j < V; j += 1024) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(lg + j);
-    const float y0 = x[0] * kLog2e, y1 = x[1] * kLog2e, y2 = x[2] * kLog2e, y3 = x[3] * kLog2e;
-    const float mx = fmaxf(fmaxf(y0, y1), fmaxf(y2, y3));
-    if (mx > m) {
-      s *= __builtin_amdgcn_exp2f(m - mx);
-      m = mx;
-    }
-    s += __builtin_amdgcn_exp2f(y0 - m) + __builtin_amdgcn_exp2f(y1 - m) +
-         __builtin_amdgcn_exp2f(y2 - m) + __builtin_amdgcn_exp2f(y3 - m);
+  for (int j = tid; j < nct; j += 256) {
+    const f32x2 ms = *reinterpret_cast<const f32x2*>(stats + (r * nct + j) * 2);
+    lse_combine(m, s, ms[0], ms[1]);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -98,7 +86,7 @@ __global__ __launch_bounds__(256) void ce_rows_fwd_kernel(const float* logits, i
   const int64_t row = row0 + r;
   const int t = targets[row];
   float loss = 0.f;
-  if (t != ignore_index) loss = (t >= 0 && t < V) ? l - lg[t] : quiet_nan();
+  if (t != ignore_index) loss = (t >= 0 && t < V) ? l - tlogit[r] : quiet_nan();
   lse[row] = l;
   loss_rows[row] = loss;
 }
@@ -143,46 +131,6 @@ __global__ __launch_bounds__(1024) void ce_reduce_kernel(const float* loss_rows,
   if (scale) *scale = cnt > 0 ? (float)((double)dloss / (double)cnt) : 0.f;
 }
 
-// dlogits[r][j] = (exp(logits[r][j] - lse_r) - [j == t_r]) * scale, bf16;
-// 0 for an ignored row, NaN for a target outside the vocabulary.  One
-// thread per 8 consecutive vocabulary entries of a row.
-__global__ __launch_bounds__(256) void ce_rows_bwd_kernel(const float* logits, int V,
-                                                          const int32_t* targets, int64_t row0,
-                                                          int rows, const float* lse,
-                                                          const float* scale, int ignore_index,
-                                                          uint16_t* dlogits) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int cpr = V / 8;
-  if (idx >= (int64_t)rows * cpr) return;
-  const int64_t r = idx / cpr;
-  const int j = (int)(idx % cpr) * 8;
-  const int64_t row = row0 + r;
-  const int t = targets[row];
-  const float sc = *scale;
-  float p[8];
-  if (t == ignore_index) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = 0.f;
-  } else {
-    const float l2 = lse[row] * kLog2e;
-    const float* lg = logits + r * V + j;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(lg);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(lg + 4);
-    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    const bool in_range = t >= 0 && t < V;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v = __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -l2));
-      if (j + i == t) v -= 1.f;
-      p[i] = in_range ? v * sc : quiet_nan();
-    }
-  }
-  u32x4 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
-  *reinterpret_cast<u32x4*>(dlogits + r * V + j) = out;
-}
-
 struct LossShape {
   int64_t L;
   int D, V, T;  // T = rows per tile (at most L)
@@ -220,14 +168,17 @@ int dh_splits(const LossShape& s) {
 }
 
 struct LossPlan {
-  size_t logits;     // [T][V] fp32
-  size_t dlogits;    // [T][V] bf16 (backward)
+  size_t stats;      // [T][ceil(V/256)] (max, sum) fp32 pairs (forward)
+  size_t tlogit;     // [T] fp32 target logits (forward)
   size_t loss_rows;  // [L] fp32 per-row loss (forward)
+  size_t dlogits;    // [T][V] bf16 (backward)
   size_t dh_acc;     // [splits][T][D] fp32 partial dh (backward, split only)
   size_t dw_acc;     // [V][D] fp32 dW accumulator (backward)
   size_t scale;      // one fp32: dloss / count (backward)
   size_t total;
 };
+
+int col_tiles(const LossShape& s) { return (s.V + 255) / 256; }
 
 LossPlan make_loss_plan(const LossShape& s, int pass) {
   LossPlan p;
@@ -239,16 +190,17 @@ LossPlan make_loss_plan(const LossShape& s, int pass) {
   };
   const size_t T = (size_t)s.T, D = (size_t)s.D, V = (size_t)s.V;
   const size_t none = (size_t)-1;
-  p.logits = take(T * V * 4);
   if (pass == UPIPE_PASS_BWD) {
+    p.stats = p.tlogit = p.loss_rows = none;
     p.dlogits = take(T * V * 2);
-    p.loss_rows = none;
     const int sp = dh_splits(s);
     p.dh_acc = sp > 1 ? take((size_t)sp * T * D * 4) : none;
     p.dw_acc = take(V * D * 4);
     p.scale = take(4);
   } else {
     p.dlogits = p.dh_acc = p.dw_acc = p.scale = none;
+    p.stats = take(T * (size_t)col_tiles(s) * 8);
+    p.tlogit = take(T * 4);
     p.loss_rows = take((size_t)s.L * 4);
   }
   p.total = off;
@@ -293,19 +245,21 @@ GemmArgs gemm_args(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ld
   return g;
 }
 
-// logits of one tile: fp32 [rows][V] = h_t W^T
-hipError_t launch_logits(const uint16_t* ht, const uint16_t* w, float* logits, int rows,
-                         const LossShape& s, hipStream_t st) {
-  return launch_gemm(GEMM_NT, EPI_STORE_F32, gemm_args(ht, s.D, w, s.D, logits, 0, rows, s.V, s.D),
-                     st);
+// logits of one tile, h_t W^T, reduced in the GEMM's epilogue: forward
+// statistics (EPI_CE_STATS) or the backward's bf16 dlogits (EPI_CE_GRAD)
+GemmArgs logits_args(const uint16_t* ht, const uint16_t* w, int rows, const LossShape& s,
+                     const int32_t* targets, int ignore_index, int64_t row0) {
+  GemmArgs g = gemm_args(ht, s.D, w, s.D, nullptr, s.V, rows, s.V, s.D);
+  g.ce_targets = targets;
+  g.ce_ignore = ignore_index;
+  g.ce_row0 = row0;
+  return g;
 }
 
 // debug mode: the tile's buffers are NaN-filled before the tile
-hipError_t debug_fill_tile(float* logits, uint16_t* dlogits, const LossShape& s, hipStream_t st) {
-  if (!g_debug_fill) return hipSuccess;
-  hipError_t e = launch_fill(logits, (size_t)s.T * s.V * 4, 0xFFFFFFFFu, st);
-  if (e != hipSuccess || !dlogits) return e;
-  return launch_fill(dlogits, (size_t)s.T * s.V * 2, 0xFFFFFFFFu, st);
+hipError_t debug_fill(void* p, size_t bytes, hipStream_t st) {
+  if (!g_debug_fill || !p) return hipSuccess;
+  return launch_fill(p, bytes, 0xFFFFFFFFu, st);
 }
 
 }  // namespace
@@ -363,14 +317,20 @@ int upipe_loss_fwd(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_
   if (rc != UPIPE_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const LossPlan p = make_loss_plan(s, UPIPE_PASS_FWD);
-  float* logits = at<float>(workspace, p.logits);
+  float* stats = at<float>(workspace, p.stats);
+  float* tlogit = at<float>(workspace, p.tlogit);
   float* loss_rows = at<float>(workspace, p.loss_rows);
+  const int nct = col_tiles(s);
   for (int64_t t0 = 0; t0 < s.L; t0 += s.T) {
     const int rows = (int)(s.L - t0 < s.T ? s.L - t0 : s.T);
-    UPIPE_TRY(debug_fill_tile(logits, nullptr, s, st));
-    UPIPE_TRY(launch_logits(h + t0 * s.D, w, logits, rows, s, st));
-    hipLaunchKernelGGL(ce_rows_fwd_kernel, dim3((unsigned)rows), dim3(256), 0, st, logits, s.V,
-                       targets, t0, ignore_index, lse, loss_rows);
+    UPIPE_TRY(debug_fill(stats, (size_t)s.T * nct * 8, st));
+    UPIPE_TRY(debug_fill(tlogit, (size_t)s.T * 4, st));
+    GemmArgs g = logits_args(h + t0 * s.D, w, rows, s, targets, ignore_index, t0);
+    g.ce_stats = stats;
+    g.ce_tlogit = tlogit;
+    UPIPE_TRY(launch_gemm(GEMM_NT, EPI_CE_STATS, g, st));
+    hipLaunchKernelGGL(ce_combine_kernel, dim3((unsigned)rows), dim3(256), 0, st, stats, nct,
+                       tlogit, s.V, targets, t0, ignore_index, lse, loss_rows);
     UPIPE_TRY(hipGetLastError());
   }
   hipLaunchKernelGGL(ce_reduce_kernel, dim3(1), dim3(1024), 0, st, loss_rows, targets, s.L,
@@ -394,7 +354,6 @@ int upipe_loss_bwd(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_
   if (rc != UPIPE_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const LossPlan p = make_loss_plan(s, UPIPE_PASS_BWD);
-  float* logits = at<float>(workspace, p.logits);
   uint16_t* dlogits = at<uint16_t>(workspace, p.dlogits);
   float* dh_acc = at<float>(workspace, p.dh_acc);
   float* dw_acc = at<float>(workspace, p.dw_acc);
@@ -407,12 +366,12 @@ int upipe_loss_bwd(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_
   for (int64_t t0 = 0; t0 < s.L; t0 += s.T) {
     const int rows = (int)(s.L - t0 < s.T ? s.L - t0 : s.T);
     const uint16_t* ht = h + t0 * D;
-    UPIPE_TRY(debug_fill_tile(logits, dlogits, s, st));
-    UPIPE_TRY(launch_logits(ht, w, logits, rows, s, st));
-    const int64_t chunks = (int64_t)rows * (V / 8);
-    hipLaunchKernelGGL(ce_rows_bwd_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
-                       st, logits, V, targets, t0, rows, lse, scale, ignore_index, dlogits);
-    UPIPE_TRY(hipGetLastError());
+    UPIPE_TRY(debug_fill(dlogits, (size_t)s.T * V * 2, st));
+    GemmArgs gl = logits_args(ht, w, rows, s, targets, ignore_index, t0);
+    gl.C = dlogits;
+    gl.ce_lse = lse;
+    gl.ce_scale = scale;
+    UPIPE_TRY(launch_gemm(GEMM_NT, EPI_CE_GRAD, gl, st));
     // dh_t = dlogits W: one split stores bf16, several store fp32 slices
     // summed in split order
     if (splits <= 1) {

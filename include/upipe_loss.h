@@ -18,10 +18,13 @@
  * memory progression in "Untied Ulysses Pushes Llama-3-8B Training to 5
  * Million Tokens" that tiles losses and MLPs along the sequence (Arctic Long
  * Sequence Training), so that no buffer of size L x vocab exists.  The
- * forward keeps one tile's fp32 logits in the workspace and returns the
- * per-row log-sum-exp; the backward recomputes each tile's logits from h and
- * that log-sum-exp, and sums dW over tiles in an fp32 accumulator held in
- * the workspace (the size of W, independent of L and of the tile).
+ * logits never reach memory in fp32: in the forward, the GEMM that forms a
+ * tile's logits reduces each row over each 256-column tile to its maximum
+ * and sum of exponentials in its epilogue, and the forward returns the
+ * per-row log-sum-exp; the backward recomputes the tile's logits and its
+ * GEMM epilogue writes the bf16 dlogits from them and that log-sum-exp; dW
+ * is summed over tiles in an fp32 accumulator held in the workspace (the
+ * size of W, independent of L and of the tile).
  *
  * Conventions where the pages are silent: the loss is the mean cross-entropy
  * of the Llama models the pages train; rows whose target is ignore_index
@@ -44,9 +47,10 @@
  *  - Supported: 1 <= L <= 2^24, hidden and vocab multiples of 128 (pad the
  *    vocabulary; padded rows of W take part in the softmax), hidden * vocab
  *    < 2^33, tile_rows >= 1 (a tile larger than L is L).
- *  - Precision: bf16 operands with fp32 accumulation; the logits are fp32,
- *    the log-sum-exp and the loss are evaluated in fp32 (the mean's sum in
- *    fp64); dlogits is rounded to bf16 between the backward's GEMMs.
+ *  - Precision: bf16 operands with fp32 accumulation; the logits are fp32
+ *    (in registers), the log-sum-exp and the loss are evaluated in fp32
+ *    (the mean's sum in fp64); dlogits is rounded to bf16 between the
+ *    backward's GEMMs.
  *  - The loss, the log-sum-exp, dh and dW are bitwise reproducible from run
  *    to run (no atomics: the mean is summed by one workgroup in a fixed
  *    order, dW accumulates tile by tile, and short tiles split dh's
@@ -65,13 +69,14 @@ extern "C" {
 #endif
 
 /*
- * Workspace size query for upipe_loss_fwd (pass = UPIPE_PASS_FWD): one
- * tile's fp32 logits [tile, vocab] and 4 bytes per row of the sequence (the
- * per-row loss); or for upipe_loss_bwd (pass = UPIPE_PASS_BWD): one tile's
- * fp32 logits and bf16 dlogits [tile, vocab], for tiles too short to give
- * the dh GEMM 256 output tiles of 256 x 256 the fp32 slices of its split
- * reduction (s [tile, hidden], s = min(ceil(256 / output tiles),
- * vocab / 512)), and the fp32 dW accumulator (4 * vocab * hidden bytes).
+ * Workspace size query for upipe_loss_fwd (pass = UPIPE_PASS_FWD): per row
+ * of a tile one fp32 (max, sum) pair per 256-column tile of the vocabulary
+ * and the target's logit, and 4 bytes per row of the sequence (the per-row
+ * loss); or for upipe_loss_bwd (pass = UPIPE_PASS_BWD): one tile's bf16
+ * dlogits [tile, vocab], for tiles too short to give the dh GEMM 256 output
+ * tiles of 256 x 256 the fp32 slices of its split reduction (s [tile,
+ * hidden], s = min(ceil(256 / output tiles), vocab / 512)), and the fp32 dW
+ * accumulator (4 * vocab * hidden bytes).
  * Returns UPIPE_OK or the error the entry point would return for these
  * shapes.  Host only.
  */

@@ -153,8 +153,9 @@ def test_ignored_rows_and_out_of_range_targets():
 
 
 def test_debug_nan_fill_changes_nothing():
-    """Debug mode NaN-fills each tile's logits (and dlogits) before the tile:
-    every output must equal the normal run's bit for bit."""
+    """Debug mode NaN-fills each tile's statistics and target logits (and
+    dlogits) before the tile: every output must equal the normal run's bit
+    for bit."""
     import headwise_chunked_context_amd as lib
 
     torch = _torch()
