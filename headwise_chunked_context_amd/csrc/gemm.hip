@@ -351,11 +351,46 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   }
   __syncthreads();  // the epilogue reuses the stages
 
-  if (EPI == EPI_ATOMIC_F32 || EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32) {
-    // fp32 accumulator [M][N]: split-K partial tiles meet by atomic adds, or
-    // each split stores its partial tile into its own [M][N] slice (summed
-    // in split order afterwards); a single split owns its elements and may
-    // also add them plainly
+  if (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32) {
+    // fp32 [M][N]: each split stores its partial tile into its own [M][N]
+    // slice (summed in split order afterwards), or a single split, which
+    // owns its elements, adds its tile.  Staged through LDS one 128-row
+    // half at a time (128 KB, the two operand stages), so every lane moves
+    // 16 bytes of one row and a wave covers whole 1 KB row segments.
+    float* C = reinterpret_cast<float*>(p.C) +
+               (EPI == EPI_STORE_F32 ? (int64_t)(tile / (gx * gy)) * p.M * p.N : 0);
+    float* Cs = reinterpret_cast<float*>(smem);
+    constexpr int FIT = 128 * (BN / 4) / NT;  // 16-byte chunks per thread per half
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              Cs[(mb * 16 + 4 * q4 + r) * BN + wn * (BN / WN) + nb * 16 + l16] = acc[mb][nb][r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < FIT; ++it) {
+        const int c = tid + NT * it;
+        const int r = c >> 6, cc = c & 63;
+        const int m = m0 + half * 128 + r, n = n0 + cc * 4;
+        if (m < p.M && n < p.N) {
+          f32x4 v = *reinterpret_cast<const f32x4*>(Cs + r * BN + cc * 4);
+          f32x4* dst = reinterpret_cast<f32x4*>(C + (int64_t)m * p.N + n);
+          if (EPI == EPI_ADD_F32) v += *dst;
+          *dst = v;
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  if (EPI == EPI_ATOMIC_F32) {
+    // fp32 accumulator [M][N]: split-K partial tiles meet by atomic adds
     float* C = reinterpret_cast<float*>(p.C);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -366,15 +401,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
         for (int r = 0; r < 4; ++r) {
           const int m = m0 + wm * (BM / WM) + mb * 16 + 4 * q4 + r;
           if (m < p.M && n < p.N) {
-            // EPI_STORE_F32 writes split s's partial tile into slice s
-            float* c = C + (int64_t)m * p.N + n +
-                       (EPI == EPI_STORE_F32 ? (int64_t)(tile / (gx * gy)) * p.M * p.N : 0);
-            if (EPI == EPI_ATOMIC_F32)
-              atomicAdd(c, acc[mb][nb][r]);
-            else if (EPI == EPI_STORE_F32)
-              *c = acc[mb][nb][r];
-            else
-              *c += acc[mb][nb][r];
+            atomicAdd(C + (int64_t)m * p.N + n, acc[mb][nb][r]);
           }
         }
       }
