@@ -442,13 +442,9 @@ def loss_sweep(lib) -> dict:
 
     base = synthetic.LOSS_WORKLOADS[22]
     out = {}
-    g = torch.Generator(device="cuda:0").manual_seed(1000 * base.wid)
     L, D, V = base.L, base.hidden, base.vocab
-    h = torch.randn(L, D, generator=g, device="cuda:0", dtype=torch.float32).to(torch.bfloat16)
-    w = (torch.randn(V, D, generator=g, device="cuda:0", dtype=torch.float32) * base.w_sigma).to(
-        torch.bfloat16)
-    t = torch.randint(0, V, (L,), generator=g, device="cuda:0", dtype=torch.int32)
-    t[::base.ignore_every] = synthetic.IGNORE_INDEX
+    dev = synthetic.make_loss_inputs_device(base)
+    h, w, t = dev["h"], dev["w"], dev["targets"]
     io = sum(x.numel() * x.element_size() for x in (h, w, t))
     for tile in (2048, 4096, 8192):
         torch.cuda.synchronize()

@@ -147,6 +147,26 @@ def make_loss_inputs(w: LossWorkload, seed_base: int | None = None) -> dict:
     }
 
 
+def make_loss_inputs_device(w: LossWorkload, device="cuda:0") -> dict:
+    """The same distributions drawn on the device by torch's generator
+    (seeded 1000 * wid), for sizes whose host draw takes minutes: h, w as
+    torch bfloat16 and targets as int32 tensors on `device`, every
+    `ignore_every`-th position set to IGNORE_INDEX.  Not the host recipe's
+    values."""
+    import torch
+
+    g = torch.Generator(device=device).manual_seed(1000 * w.wid)
+    h = torch.randn(w.L, w.hidden, generator=g, device=device, dtype=torch.float32)
+    if w.h_sigma != 1.0:
+        h.mul_(w.h_sigma)
+    wt = torch.randn(w.vocab, w.hidden, generator=g, device=device, dtype=torch.float32)
+    wt.mul_(w.w_sigma)
+    t = torch.randint(0, w.vocab, (w.L,), generator=g, device=device, dtype=torch.int32)
+    if w.ignore_every > 0:
+        t[::w.ignore_every] = IGNORE_INDEX
+    return {"h": h.to(torch.bfloat16), "w": wt.to(torch.bfloat16), "targets": t}
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)

@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import synthetic
-from _helpers import f64, from_dev_bf16, from_dev_f32, rel_l2, to_dev
+from _helpers import f64, from_dev_bf16, from_dev_bf16_f32, from_dev_f32, rel_l2, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -171,3 +171,88 @@ def test_debug_nan_fill_changes_nothing():
         assert torch.equal(ref[k].view(torch.int32), dbg[k].view(torch.int32)), k
     for k in ("dh", "dw"):
         assert torch.equal(ref[k].view(torch.int16), dbg[k].view(torch.int16)), k
+
+
+# ------------------------------------------------ the Llama-3-8B output projection
+def _bf16_host(t):
+    """torch bf16 on the device -> float64 numpy (exact)."""
+    return from_dev_bf16(t)
+
+
+def _run_dev(dev, tile, dloss=1.0):
+    import headwise_chunked_context_amd as lib
+
+    torch = _torch()
+    loss, lse = lib.loss_fwd(dev["h"], dev["w"], dev["targets"], tile, IGN)
+    dh, dw = lib.loss_bwd(dev["h"], dev["w"], dev["targets"], lse, dloss, tile, IGN)
+    torch.cuda.synchronize()
+    return dict(loss=loss, lse=lse, dh=dh, dw=dw)
+
+
+def test_llama3_8b_output_projection_short_sequence():
+    """hidden 4096 and vocabulary 128256 (the Llama-3-8B output projection) at
+    L 512 in ragged tiles of 200, every output against the full oracle
+    (inputs drawn on the device, copied to the host for the oracle)."""
+    _torch()
+    w = synthetic.LOSS_WORKLOADS[22].with_(L=512, tile_rows=200)
+    dev = synthetic.make_loss_inputs_device(w)
+    print("llama3-8b output projection L=512: GPU", flush=True)
+    g = _run_dev(dev, w.tile_rows)
+    h, wt = _bf16_host(dev["h"]), _bf16_host(dev["w"])
+    t = dev["targets"].cpu().numpy()
+    print("llama3-8b output projection L=512: oracle", flush=True)
+    rloss, rlse = oracle.loss_fwd(h, wt, t, IGN, w.tile_rows)
+    rdh, rdw = oracle.loss_bwd(h, wt, t, IGN, rlse, 1.0, w.tile_rows)
+    gloss = float(from_dev_f32(g["loss"])[0])
+    errs = {"loss": abs(gloss - rloss), "lse": float(np.max(np.abs(from_dev_f32(g["lse"]) - rlse))),
+            "dh_rel": rel_l2(from_dev_bf16(g["dh"]), rdh), "dw_rel": rel_l2(from_dev_bf16(g["dw"]), rdw)}
+    print("llama3-8b output projection L=512", f"loss {gloss:.6f} ref {rloss:.6f}",
+          {k: f"{v:.3e}" for k, v in errs.items()}, flush=True)
+    assert errs["loss"] <= LOSS_ABS and errs["lse"] <= LSE_ABS, errs
+    assert errs["dh_rel"] <= GRAD_REL and errs["dw_rel"] <= GRAD_REL, errs
+
+
+def test_llama3_8b_output_projection_full_length():
+    """The benchmarked size, L 32768 in tiles of 4096 (the [tile, vocab]
+    buffers hold 2^29 elements): the oracle on 24 sampled rows (their
+    log-sum-exp, and their dh with the full sequence's count of counted rows
+    in the scale), and the property that holds at any size: each counted
+    row's dlogits sums to zero over the vocabulary, so dW summed over its
+    vocabulary rows vanishes up to the bf16 roundings.  Those are the
+    rounding of each row's target entry of dlogits (about -scale, RMS
+    relative error 2^-7 / sqrt(12) = 2.3e-3) and of the target rows of dW,
+    so a column sum has RMS ~2.3e-3 * scale * sqrt(2 count) ~ 1.8e-5 (scale
+    = 1 / count, count ~ 30720), ~4 times that at the maximum over 4096
+    columns: gate 3e-4.  A dropped one-hot or a wrong scale leaves
+    ~sqrt(count) / count ~ 6e-3 per column."""
+    torch = _torch()
+    w = synthetic.LOSS_WORKLOADS[22]
+    dev = synthetic.make_loss_inputs_device(w)
+    print("llama3-8b output projection L=32768: GPU", flush=True)
+    g = _run_dev(dev, w.tile_rows)
+    t = dev["targets"].cpu().numpy()
+    count = int((t != IGN).sum())
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, w.tile_rows - 1, w.tile_rows, w.L - 1],
+                                     rng.choice(w.L, size=19, replace=False)]))
+    wt = from_dev_bf16_f32(dev["w"]).astype(np.float64)
+    hs = _bf16_host(dev["h"][torch.from_numpy(rows).to("cuda:0")])
+    print(f"llama3-8b output projection L=32768: oracle on {rows.size} rows", flush=True)
+    _, rlse = oracle.loss_fwd(hs, wt, t[rows], IGN, rows.size)
+    n_sample = int((t[rows] != IGN).sum())
+    # the sample's own count enters the oracle's scale; rescale dloss so the
+    # scale is 1 / (the full sequence's count)
+    rdh, _ = oracle.loss_bwd(hs, wt, t[rows], IGN, rlse, n_sample / count if n_sample else 0.0, rows.size)
+    del wt
+    glse = from_dev_f32(g["lse"])[rows]
+    gdh = from_dev_bf16(g["dh"][torch.from_numpy(rows).to("cuda:0")])
+    e_lse = float(np.max(np.abs(glse - rlse)))
+    e_dh = rel_l2(gdh, rdh)
+    colsum = g["dw"].float().sum(dim=0).abs().max().item()
+    loss = float(from_dev_f32(g["loss"])[0])
+    print(f"llama3-8b output projection L=32768: loss {loss:.6f}, sampled lse max {e_lse:.3e}, "
+          f"sampled dh rel {e_dh:.3e}, max |sum_v dW[v]| {colsum:.3e}", flush=True)
+    # logits ~N(0, 1.28^2): the mean loss is near log(vocab) + 1.28^2 / 2
+    assert np.isfinite(loss) and abs(loss - np.log(w.vocab)) < 2.0
+    assert e_lse <= LSE_ABS and e_dh <= GRAD_REL
+    assert colsum <= 3e-4
