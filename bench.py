@@ -46,6 +46,14 @@ the Llama-3-8B shape (hidden 4096, intermediate 14336) over L 32768, forward
 loss_workloads: the sequence-tiled cross-entropy loss of the same stack at
 the Llama-3-8B output projection (hidden 4096, vocabulary 128256) over
 L 32768, forward + backward at tiles of 2048, 4096 and 8192 rows.
+
+mfma_probe: the bf16 MFMA rate this chip sustains in the same run (after
+the timed steps), from a probe kernel of four independent
+v_mfma_f32_32x32x16_bf16 chains per wave at two waves per SIMD, on N(0, 1)
+operands (the layer's data) and on constant operands, with the clock the
+waves ran at (shader over constant clock ticks).  Under MFMA load the chip is
+power-limited and the clock depends on the data; the roofline fraction stays
+against the published 2.5 PFLOP/s.
 """
 from __future__ import annotations
 
@@ -483,6 +491,40 @@ def loss_sweep(lib) -> dict:
     return out
 
 
+def mfma_probe(lib) -> dict:
+    """Sustained bf16 MFMA rate and clock on N(0, 1) and on constant
+    operands (about 80 ms each)."""
+    import torch
+
+    from headwise_chunked_context_amd.binding import PROBE_FLOP_PER_ROUND
+
+    g = torch.Generator(device="cuda:0").manual_seed(11)
+    out = {"kernel": "v_mfma_f32_32x32x16_bf16, 4 independent accumulator chains per wave over 8 "
+                     "operand pairs, 512 workgroups x 4 waves (2 waves per SIMD)"}
+    wg, iters = 512, 60000
+    for kind in ("normal_operands", "constant_operands"):
+        if kind == "normal_operands":
+            ops = torch.randn(8 << 20, generator=g, device="cuda:0").to(torch.bfloat16)
+        else:
+            ops = torch.full((8 << 20,), 1.0, device="cuda:0", dtype=torch.bfloat16)
+        lib.probe_mfma(ops, 200, wg)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        _, clocks = lib.probe_mfma(ops, iters, wg)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        tflops = wg * 4 * iters * PROBE_FLOP_PER_ROUND / (ms * 1e-3) / 1e12
+        ck = clocks.view(-1, 2).double()
+        ghz = float((ck[:, 0] / ck[:, 1]).mean()) * 0.1   # constant clock: 100 MHz
+        out[kind] = {"tflops": round(tflops, 1), "clock_ghz": round(ghz, 3),
+                     "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "ms": round(ms, 2)}
+        print(f"bench: mfma probe, {kind}: {tflops:.0f} TFLOP/s at {ghz:.2f} GHz", file=sys.stderr,
+              flush=True)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -616,6 +658,7 @@ def main() -> int:
         "peak_allocated_gib": round(mem0 / 2**30, 3),
         "hbm_passes": r["hbm"],
     }
+    out["mfma_probe"] = mfma_probe(lib)
     if not args.no_sweep and not args.seq_len and args.workload == 2 and not args.chunk:
         del x, wq, wo, dy
         out["workloads"] = sweep(lib)

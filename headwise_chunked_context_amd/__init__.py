@@ -40,6 +40,7 @@ from .binding import (  # noqa: F401
     mlp_fwd,
     mlp_workspace_bytes,
     pipeline_enable,
+    probe_mfma,
     pipeline_enabled,
     profile_enable,
     profile_read,

@@ -28,8 +28,8 @@ PASS_FWD_PIPELINED = 3
 PASS_BWD_PIPELINED = 4
 _pipeline = False
 
-# names declared in include/upipe_attn.h, include/upipe_mlp.h and
-# include/upipe_loss.h
+# names declared in include/upipe_attn.h, include/upipe_mlp.h,
+# include/upipe_loss.h and include/upipe_probe.h
 EXPORTS = (
     "upipe_attn_workspace_bytes",
     "upipe_attn_fwd",
@@ -44,6 +44,7 @@ EXPORTS = (
     "upipe_loss_choose_tile",
     "upipe_loss_fwd",
     "upipe_loss_bwd",
+    "upipe_probe_mfma",
     "upipe_profile_enable",
     "upipe_profile_read",
     "upipe_pipeline_enable",
@@ -123,6 +124,8 @@ def lib() -> ctypes.CDLL:
     L.upipe_loss_bwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp,
                                  vp, sz, vp]
     L.upipe_loss_bwd.restype = ctypes.c_int
+    L.upipe_probe_mfma.argtypes = [vp, sz, i32, i32, vp, vp, vp]
+    L.upipe_probe_mfma.restype = ctypes.c_int
     L.upipe_strerror.argtypes = [ctypes.c_int]
     L.upipe_strerror.restype = ctypes.c_char_p
     L.upipe_version.argtypes = []
@@ -516,3 +519,25 @@ def loss_bwd(h, w, targets, lse, dloss: float, tile_rows: int, ignore_index: int
     if rc != UPIPE_OK:
         raise UpipeError(rc, "upipe_loss_bwd")
     return dh, dw
+
+
+# ---------------------------------------------------------------- MFMA probe
+PROBE_FLOP_PER_ROUND = 32 * 32 * 32 * 16 * 2   # 32 MFMAs 32x32x16 per wave and round
+
+
+def probe_mfma(operands, iters: int, workgroups: int, stream=None):
+    """Launch the sustained bf16 MFMA probe over `operands` (a bf16 device
+    tensor of at least 16 MiB).  Returns (sink, clocks) device tensors; the
+    caller times the launch.  FLOPs = workgroups * 4 * iters *
+    PROBE_FLOP_PER_ROUND; clock = clocks[0::2] / clocks[1::2] * 100 MHz."""
+    import torch
+
+    if not operands.is_cuda or operands.dtype != torch.bfloat16 or not operands.is_contiguous():
+        raise ValueError("operands must be a contiguous bf16 device tensor")
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device=operands.device)
+    clocks = torch.empty(workgroups * 4 * 2, dtype=torch.int64, device=operands.device)
+    rc = lib().upipe_probe_mfma(_ptr(operands), operands.numel() * 2, iters, workgroups, _ptr(sink),
+                                _ptr(clocks), _stream(stream))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_probe_mfma")
+    return sink, clocks

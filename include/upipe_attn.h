@@ -292,7 +292,8 @@ int upipe_pipeline_enable(int on);
 
 /*
  * Debug mode (off by default), a check for workspace reuse between chunks:
- * before each chunk (and each tile of upipe_mlp_fwd / upipe_mlp_bwd) the
+ * before each chunk (and each tile of upipe_mlp_fwd / upipe_mlp_bwd and
+ * upipe_loss_fwd / upipe_loss_bwd) the
  * library fills that chunk's workspace buffers with 0xFF bytes (NaN in
  * bf16, fp16 and fp32) by a fill kernel on the stream that then writes
  * them, so a kernel that read a buffer before the chunk wrote it, or read a
