@@ -45,7 +45,8 @@ the Llama-3-8B shape (hidden 4096, intermediate 14336) over L 32768, forward
 
 loss_workloads: the sequence-tiled cross-entropy loss of the same stack at
 the Llama-3-8B output projection (hidden 4096, vocabulary 128256) over
-L 32768, forward + backward at tiles of 2048, 4096 and 8192 rows.
+L 32768, forward + backward at tiles of 2048, 4096 and 8192 rows, as two
+passes and as the fused forward-backward.
 
 mfma_probe: the bf16 MFMA rate this chip sustains in the same run (after
 the timed steps), from a probe kernel of four independent
@@ -440,10 +441,10 @@ def mlp_sweep(lib) -> dict:
 def loss_sweep(lib) -> dict:
     """The sequence-tiled cross-entropy loss at the Llama-3-8B output
     projection (hidden 4096, vocabulary 128256) over L 32768, forward +
-    backward, at several tile sizes: ms per step, TFLOP/s of model work
-    (6 L hidden vocab: forward 2, backward 4; the backward's recompute of
-    the logits, 2 more, is executed, not counted), workspace and allocator
-    peak."""
+    backward, at several tile sizes, as two passes and fused: ms per step,
+    TFLOP/s of model work (6 L hidden vocab: forward 2, backward 4; the
+    separate backward's recompute of the logits, 2 more, is executed, not
+    counted), workspace and allocator peak."""
     import torch
 
     import synthetic
@@ -454,15 +455,22 @@ def loss_sweep(lib) -> dict:
     dev = synthetic.make_loss_inputs_device(base)
     h, w, t = dev["h"], dev["w"], dev["targets"]
     io = sum(x.numel() * x.element_size() for x in (h, w, t))
-    for tile in (2048, 4096, 8192):
+    for tile, fused in ((2048, False), (4096, False), (8192, False), (2048, True), (4096, True),
+                        (8192, True)):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
-        ws_f = lib.loss_workspace_bytes(L, D, V, tile, lib.PASS_FWD)
-        ws_b = lib.loss_workspace_bytes(L, D, V, tile, lib.PASS_BWD)
+        if fused:
+            ws_f = ws_b = lib.loss_workspace_bytes(L, D, V, tile, lib.PASS_FWD_BWD)
+        else:
+            ws_f = lib.loss_workspace_bytes(L, D, V, tile, lib.PASS_FWD)
+            ws_b = lib.loss_workspace_bytes(L, D, V, tile, lib.PASS_BWD)
         ws = torch.empty(max(ws_f, ws_b), dtype=torch.uint8, device="cuda:0")
 
         def step():
+            if fused:
+                lib.loss_fwd_bwd(h, w, t, 1.0, tile, synthetic.IGNORE_INDEX, workspace=ws)
+                return
             _, lse = lib.loss_fwd(h, w, t, tile, synthetic.IGNORE_INDEX, workspace=ws)
             lib.loss_bwd(h, w, t, lse, 1.0, tile, synthetic.IGNORE_INDEX, workspace=ws)
 
@@ -476,9 +484,10 @@ def loss_sweep(lib) -> dict:
         ms = (time.perf_counter() - t0) * 1e3 / steps
         peak = torch.cuda.max_memory_allocated()
         del ws
-        key = f"llama3_8b_loss_hidden4096_vocab128256_L32768_tile{tile}"
+        key = f"llama3_8b_loss_hidden4096_vocab128256_L32768_tile{tile}" + ("_fused" if fused else "")
         out[key] = {
             "seq_len": L, "hidden": D, "vocab": V, "tile_rows": tile, "steps": steps, "warmup": 1,
+            "mode": "fused forward-backward" if fused else "forward, then backward",
             "ms_per_step": round(ms, 3),
             "tflops": round(6.0 * L * D * V / (ms * 1e-3) / 1e12, 2),
             "workspace_gib": {"fwd": round(ws_f / 2**30, 4), "bwd": round(ws_b / 2**30, 4)},

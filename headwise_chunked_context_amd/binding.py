@@ -26,6 +26,7 @@ PASS_BWD = 1
 PASS_BWD_RECOMPUTE = 2
 PASS_FWD_PIPELINED = 3
 PASS_BWD_PIPELINED = 4
+PASS_FWD_BWD = 5   # the loss's fused forward-backward
 _pipeline = False
 
 # names declared in include/upipe_attn.h, include/upipe_mlp.h,
@@ -44,6 +45,7 @@ EXPORTS = (
     "upipe_loss_choose_tile",
     "upipe_loss_fwd",
     "upipe_loss_bwd",
+    "upipe_loss_fwd_bwd",
     "upipe_probe_mfma",
     "upipe_profile_enable",
     "upipe_profile_read",
@@ -124,6 +126,9 @@ def lib() -> ctypes.CDLL:
     L.upipe_loss_bwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp,
                                  vp, sz, vp]
     L.upipe_loss_bwd.restype = ctypes.c_int
+    L.upipe_loss_fwd_bwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, vp,
+                                     vp, vp, vp, sz, vp]
+    L.upipe_loss_fwd_bwd.restype = ctypes.c_int
     L.upipe_probe_mfma.argtypes = [vp, sz, i32, i32, vp, vp, vp]
     L.upipe_probe_mfma.restype = ctypes.c_int
     L.upipe_strerror.argtypes = [ctypes.c_int]
@@ -519,6 +524,27 @@ def loss_bwd(h, w, targets, lse, dloss: float, tile_rows: int, ignore_index: int
     if rc != UPIPE_OK:
         raise UpipeError(rc, "upipe_loss_bwd")
     return dh, dw
+
+
+def loss_fwd_bwd(h, w, targets, dloss: float, tile_rows: int, ignore_index: int = -100,
+                 workspace=None, stream=None):
+    """Forward and backward of the tiled loss in one pass (dloss known up
+    front).  Returns (loss [1] fp32, lse [L] fp32, dh, dw)."""
+    import torch
+
+    L, hidden, vocab = _check_loss(h, w, targets)
+    loss = torch.empty(1, dtype=torch.float32, device=h.device)
+    lse = torch.empty(L, dtype=torch.float32, device=h.device)
+    dh = torch.empty_like(h)
+    dw = torch.empty_like(w)
+    ws = _workspace(loss_workspace_bytes(L, hidden, vocab, tile_rows, PASS_FWD_BWD), h.device,
+                    workspace)
+    rc = lib().upipe_loss_fwd_bwd(L, hidden, vocab, tile_rows, _ptr(h), _ptr(w), _ptr(targets),
+                                  ignore_index, float(dloss), _ptr(loss), _ptr(lse), _ptr(dh),
+                                  _ptr(dw), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if rc != UPIPE_OK:
+        raise UpipeError(rc, "upipe_loss_fwd_bwd")
+    return loss, lse, dh, dw
 
 
 # ---------------------------------------------------------------- MFMA probe

@@ -472,6 +472,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
           }
           const int t = p.ce_targets[p.ce_row0 + m];
           if (t >= n && t < n + 8 && t < p.N) p.ce_tlogit[m] = src[t - n];
+          if (p.ce_logits16 && n < p.N) {
+            // the fused forward-backward keeps the logits in fp16 (finite
+            // values beyond +-65504 saturate) for its dlogits pass
+            u32x4 h16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h16[i] = pack_f16x2_sat(src[2 * i], src[2 * i + 1]);
+            *reinterpret_cast<u32x4*>(p.ce_logits16 + (int64_t)m * p.N + n) = h16;
+          }
         }
         continue;
       }

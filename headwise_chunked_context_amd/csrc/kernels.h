@@ -89,6 +89,8 @@ struct GemmArgs {
   int64_t ce_row0;
   float* ce_stats;
   float* ce_tlogit;
+  uint16_t* ce_logits16;  // EPI_CE_STATS, optional: [M][N] fp16 logits
+
   const float* ce_lse;
   const float* ce_scale;
   RopeTable rope;

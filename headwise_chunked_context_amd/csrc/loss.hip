@@ -131,6 +131,44 @@ __global__ __launch_bounds__(1024) void ce_reduce_kernel(const float* loss_rows,
   if (scale) *scale = cnt > 0 ? (float)((double)dloss / (double)cnt) : 0.f;
 }
 
+// In place, fp16 logits -> bf16 dlogits = (exp(logit - lse_r) - [j == t_r])
+// * scale (0 for an ignored row, NaN for a target outside the vocabulary);
+// one thread per 8 consecutive vocabulary entries of a row, each reading and
+// writing only its own 16 bytes.
+__global__ __launch_bounds__(256) void ce_grad_f16_kernel(uint16_t* buf, int V,
+                                                          const int32_t* targets, int64_t row0,
+                                                          int rows, const float* lse,
+                                                          const float* scale, int ignore_index) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = V / 8;
+  if (idx >= (int64_t)rows * cpr) return;
+  const int64_t r = idx / cpr;
+  const int j = (int)(idx % cpr) * 8;
+  const int64_t row = row0 + r;
+  const int t = targets[row];
+  u32x4* p = reinterpret_cast<u32x4*>(buf + r * V + j);
+  float v[8];
+  if (t == ignore_index) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  } else {
+    const u32x4 x = *p;
+    const float l2 = lse[row] * kLog2e, sc = *scale;
+    const bool in_range = t >= 0 && t < V;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float lg = (i & 1) ? f16_hi(x[i >> 1]) : f16_lo(x[i >> 1]);
+      float e = __builtin_amdgcn_exp2f(fmaf(lg, kLog2e, -l2));
+      if (j + i == t) e -= 1.f;
+      v[i] = in_range ? e * sc : quiet_nan();
+    }
+  }
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  *p = out;
+}
+
 struct LossShape {
   int64_t L;
   int D, V, T;  // T = rows per tile (at most L)
@@ -190,7 +228,18 @@ LossPlan make_loss_plan(const LossShape& s, int pass) {
   };
   const size_t T = (size_t)s.T, D = (size_t)s.D, V = (size_t)s.V;
   const size_t none = (size_t)-1;
-  if (pass == UPIPE_PASS_BWD) {
+  if (pass == UPIPE_PASS_FWD_BWD) {
+    // forward statistics and per-row loss, and the backward's buffers; the
+    // [T][V] tile holds fp16 logits, then (in place) bf16 dlogits
+    p.stats = take(T * (size_t)col_tiles(s) * 8);
+    p.tlogit = take(T * 4);
+    p.loss_rows = take((size_t)s.L * 4);
+    p.dlogits = take(T * V * 2);
+    const int sp = dh_splits(s);
+    p.dh_acc = sp > 1 ? take((size_t)sp * T * D * 4) : none;
+    p.dw_acc = take(V * D * 4);
+    p.scale = take(4);
+  } else if (pass == UPIPE_PASS_BWD) {
     p.stats = p.tlogit = p.loss_rows = none;
     p.dlogits = take(T * V * 2);
     const int sp = dh_splits(s);
@@ -256,6 +305,32 @@ GemmArgs logits_args(const uint16_t* ht, const uint16_t* w, int rows, const Loss
   return g;
 }
 
+// the weight-side products of one tile's bf16 dlogits [rows][V]:
+//   dh_t = dlogits W   (NN; one split stores bf16, several store fp32
+//                       slices summed in split order)
+//   dW  += dlogits^T h_t  (TN, one split: the first tile stores, later ones
+//                       add with plain stores; the tiles run in order on one
+//                       stream)
+hipError_t grads_of_tile(const uint16_t* dlogits, const uint16_t* ht, const uint16_t* w,
+                         uint16_t* dh_t, float* dh_acc, float* dw_acc, int rows, int splits,
+                         const LossShape& s, bool first, hipStream_t st) {
+  const int D = s.D, V = s.V;
+  hipError_t e;
+  if (splits <= 1) {
+    e = launch_gemm(GEMM_NN, EPI_STORE_BF16, gemm_args(dlogits, V, w, D, dh_t, D, rows, D, V), st);
+  } else {
+    GemmArgs g = gemm_args(dlogits, V, w, D, dh_acc, 0, rows, D, V);
+    g.k_per_split = gemm_k_per_split(V, splits);
+    const int used = (V + g.k_per_split - 1) / g.k_per_split;
+    e = launch_gemm(GEMM_NN, EPI_STORE_F32, g, st);
+    if (e == hipSuccess) e = launch_sum_slices(dh_acc, used, rows, D, dh_t, D, st);
+  }
+  if (e != hipSuccess) return e;
+  GemmArgs g = gemm_args(dlogits, V, ht, D, dw_acc, 0, V, D, rows);
+  g.k_per_split = gemm_k_per_split(rows, 1);
+  return launch_gemm(GEMM_TN, first ? EPI_STORE_F32 : EPI_ADD_F32, g, st);
+}
+
 // debug mode: the tile's buffers are NaN-filled before the tile
 hipError_t debug_fill(void* p, size_t bytes, hipStream_t st) {
   if (!g_debug_fill || !p) return hipSuccess;
@@ -268,7 +343,8 @@ extern "C" {
 
 int upipe_loss_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_rows,
                                int32_t pass, size_t* bytes) {
-  if (!bytes || (pass != UPIPE_PASS_FWD && pass != UPIPE_PASS_BWD)) return UPIPE_EINVAL;
+  if (!bytes || (pass != UPIPE_PASS_FWD && pass != UPIPE_PASS_BWD && pass != UPIPE_PASS_FWD_BWD))
+    return UPIPE_EINVAL;
   LossShape s;
   const int rc = check_loss_shape(seq_len, hidden, vocab, tile_rows, &s);
   if (rc != UPIPE_OK) return rc;
@@ -278,7 +354,9 @@ int upipe_loss_workspace_bytes(int64_t seq_len, int32_t hidden, int32_t vocab, i
 
 int upipe_loss_choose_tile(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t pass,
                            size_t budget_bytes, int32_t* tile_rows, size_t* bytes) {
-  if (!tile_rows || !bytes || (pass != UPIPE_PASS_FWD && pass != UPIPE_PASS_BWD)) return UPIPE_EINVAL;
+  if (!tile_rows || !bytes ||
+      (pass != UPIPE_PASS_FWD && pass != UPIPE_PASS_BWD && pass != UPIPE_PASS_FWD_BWD))
+    return UPIPE_EINVAL;
   LossShape s;
   int rc = check_loss_shape(seq_len, hidden, vocab, 1, &s);
   if (rc != UPIPE_OK) return rc;
@@ -372,24 +450,67 @@ int upipe_loss_bwd(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_
     gl.ce_lse = lse;
     gl.ce_scale = scale;
     UPIPE_TRY(launch_gemm(GEMM_NT, EPI_CE_GRAD, gl, st));
-    // dh_t = dlogits W: one split stores bf16, several store fp32 slices
-    // summed in split order
-    if (splits <= 1) {
-      UPIPE_TRY(launch_gemm(GEMM_NN, EPI_STORE_BF16,
-                            gemm_args(dlogits, V, w, D, dh + t0 * D, D, rows, D, V), st));
-    } else {
-      GemmArgs g = gemm_args(dlogits, V, w, D, dh_acc, 0, rows, D, V);
-      g.k_per_split = gemm_k_per_split(V, splits);
-      const int used = (V + g.k_per_split - 1) / g.k_per_split;
-      UPIPE_TRY(launch_gemm(GEMM_NN, EPI_STORE_F32, g, st));
-      UPIPE_TRY(launch_sum_slices(dh_acc, used, rows, D, dh + t0 * D, D, st));
-    }
-    // dW += dlogits^T h_t, one split: the first tile stores, later ones add
-    // (plain stores; the tiles run in order on one stream)
-    GemmArgs g = gemm_args(dlogits, V, ht, D, dw_acc, 0, V, D, rows);
-    g.k_per_split = gemm_k_per_split(rows, 1);
-    UPIPE_TRY(launch_gemm(GEMM_TN, t0 == 0 ? EPI_STORE_F32 : EPI_ADD_F32, g, st));
+    UPIPE_TRY(grads_of_tile(dlogits, ht, w, dh + t0 * D, dh_acc, dw_acc, rows, splits, s, t0 == 0, st));
   }
+  RowSegments ident;
+  memset(&ident, 0, sizeof(ident));
+  UPIPE_TRY(launch_acc_to_bf16(dw_acc, V, D, dw, D, ident, st));
+  return UPIPE_OK;
+}
+
+int upipe_loss_fwd_bwd(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_rows,
+                       const uint16_t* h, const uint16_t* w, const int32_t* targets,
+                       int32_t ignore_index, float dloss, float* loss, float* lse, uint16_t* dh,
+                       uint16_t* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  LossShape s;
+  int rc = check_loss_shape(seq_len, hidden, vocab, tile_rows, &s);
+  if (rc != UPIPE_OK) return rc;
+  if (!h || !w || !targets || !loss || !lse || !dh || !dw) return UPIPE_EINVAL;
+  if (!aligned16(h) || !aligned16(w) || !aligned4(targets) || !aligned4(loss) || !aligned4(lse) ||
+      !aligned16(dh) || !aligned16(dw))
+    return UPIPE_EINVAL;
+  rc = check_ws(s, UPIPE_PASS_FWD_BWD, workspace, workspace_bytes);
+  if (rc != UPIPE_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const LossPlan p = make_loss_plan(s, UPIPE_PASS_FWD_BWD);
+  float* stats = at<float>(workspace, p.stats);
+  float* tlogit = at<float>(workspace, p.tlogit);
+  float* loss_rows = at<float>(workspace, p.loss_rows);
+  uint16_t* dlogits = at<uint16_t>(workspace, p.dlogits);
+  float* dh_acc = at<float>(workspace, p.dh_acc);
+  float* dw_acc = at<float>(workspace, p.dw_acc);
+  float* scale = at<float>(workspace, p.scale);
+  const int D = s.D, V = s.V, nct = col_tiles(s);
+  const int splits = dh_acc ? dh_splits(s) : 1;
+  // the count of counted rows (hence dloss / count) depends on the targets
+  // only, so the gradients of each tile follow its forward at once
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3(1), dim3(1024), 0, st, (const float*)nullptr, targets,
+                     s.L, ignore_index, dloss, (float*)nullptr, scale);
+  UPIPE_TRY(hipGetLastError());
+  for (int64_t t0 = 0; t0 < s.L; t0 += s.T) {
+    const int rows = (int)(s.L - t0 < s.T ? s.L - t0 : s.T);
+    const uint16_t* ht = h + t0 * D;
+    UPIPE_TRY(debug_fill(stats, (size_t)s.T * nct * 8, st));
+    UPIPE_TRY(debug_fill(tlogit, (size_t)s.T * 4, st));
+    UPIPE_TRY(debug_fill(dlogits, (size_t)s.T * V * 2, st));
+    // logits once: row statistics, target logits and fp16 logits
+    GemmArgs g = logits_args(ht, w, rows, s, targets, ignore_index, t0);
+    g.ce_stats = stats;
+    g.ce_tlogit = tlogit;
+    g.ce_logits16 = dlogits;
+    UPIPE_TRY(launch_gemm(GEMM_NT, EPI_CE_STATS, g, st));
+    hipLaunchKernelGGL(ce_combine_kernel, dim3((unsigned)rows), dim3(256), 0, st, stats, nct,
+                       tlogit, V, targets, t0, ignore_index, lse, loss_rows);
+    UPIPE_TRY(hipGetLastError());
+    const int64_t chunks = (int64_t)rows * (V / 8);
+    hipLaunchKernelGGL(ce_grad_f16_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st,
+                       dlogits, V, targets, t0, rows, lse, scale, ignore_index);
+    UPIPE_TRY(hipGetLastError());
+    UPIPE_TRY(grads_of_tile(dlogits, ht, w, dh + t0 * D, dh_acc, dw_acc, rows, splits, s, t0 == 0, st));
+  }
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3(1), dim3(1024), 0, st, loss_rows, targets, s.L,
+                     ignore_index, 0.f, loss, (float*)nullptr);
+  UPIPE_TRY(hipGetLastError());
   RowSegments ident;
   memset(&ident, 0, sizeof(ident));
   UPIPE_TRY(launch_acc_to_bf16(dw_acc, V, D, dw, D, ident, st));

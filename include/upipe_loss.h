@@ -64,6 +64,9 @@
 
 #include "upipe_attn.h"
 
+/* pass value of the workspace query and tile choice for upipe_loss_fwd_bwd */
+#define UPIPE_PASS_FWD_BWD 5
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -76,7 +79,9 @@ extern "C" {
  * dlogits [tile, vocab], for tiles too short to give the dh GEMM 256 output
  * tiles of 256 x 256 the fp32 slices of its split reduction (s [tile,
  * hidden], s = min(ceil(256 / output tiles), vocab / 512)), and the fp32 dW
- * accumulator (4 * vocab * hidden bytes).
+ * accumulator (4 * vocab * hidden bytes); or for upipe_loss_fwd_bwd (pass
+ * = UPIPE_PASS_FWD_BWD): the forward's buffers and the backward's (its
+ * [tile, vocab] 2-byte tile first holds fp16 logits, then the bf16 dlogits).
  * Returns UPIPE_OK or the error the entry point would return for these
  * shapes.  Host only.
  */
@@ -121,6 +126,28 @@ int upipe_loss_bwd(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_
                    const uint16_t* h, const uint16_t* w, const int32_t* targets,
                    int32_t ignore_index, const float* lse, float dloss, uint16_t* dh,
                    uint16_t* dw, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward and backward in one pass, for a caller that knows dloss when the
+ * forward runs (e.g. 1 for loss.backward(), or a fixed loss scale): the
+ * outputs of upipe_loss_fwd and of upipe_loss_bwd with that dloss.  Each
+ * tile's logits are formed once instead of twice: the logits GEMM's epilogue
+ * also stores them in fp16 (finite values beyond +-65504 saturate), and an
+ * in-place pass turns them into the bf16 dlogits, so a quarter of the
+ * GEMM work of the separate passes is saved for no extra memory.  The loss
+ * and lse equal upipe_loss_fwd's bit for bit; dh and dW differ from
+ * upipe_loss_bwd's by the fp16 rounding of the logits (relative 2^-11 *
+ * |logit| in each probability, below dlogits' own bf16 rounding for
+ * |logit| < 4).
+ *  h, w, targets, ignore_index, dloss  as above
+ *  loss, lse   out, as upipe_loss_fwd
+ *  dh, dw      out, as upipe_loss_bwd
+ *  workspace   at least the UPIPE_PASS_FWD_BWD query size; contents ignored
+ */
+int upipe_loss_fwd_bwd(int64_t seq_len, int32_t hidden, int32_t vocab, int32_t tile_rows,
+                       const uint16_t* h, const uint16_t* w, const int32_t* targets,
+                       int32_t ignore_index, float dloss, float* loss, float* lse, uint16_t* dh,
+                       uint16_t* dw, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -256,3 +256,61 @@ def test_llama3_8b_output_projection_full_length():
     assert np.isfinite(loss) and abs(loss - np.log(w.vocab)) < 2.0
     assert e_lse <= LSE_ABS and e_dh <= GRAD_REL
     assert colsum <= 3e-4
+
+
+# ------------------------------------------------ fused forward-backward
+def run_fused(inp, tile, dloss=1.0):
+    import headwise_chunked_context_amd as lib
+
+    torch = _torch()
+    h, w = to_dev(inp["h"]), to_dev(inp["w"])
+    t = targets_dev(inp["targets"])
+    loss, lse, dh, dw = lib.loss_fwd_bwd(h, w, t, dloss, tile, IGN)
+    torch.cuda.synchronize()
+    return dict(loss=loss, lse=lse, dh=dh, dw=dw)
+
+
+@pytest.mark.parametrize("L,D,V,tile,dloss", [
+    (1000, 256, 1024, 256, 1.0),
+    (777, 384, 640, 300, 0.37),
+    (3, 256, 384, 2, 1.0),
+    (129, 128, 256, 4096, 1.0),
+])
+def test_fused_forward_backward_matches_oracle(L, D, V, tile, dloss):
+    """The fused pass against the oracle with the separate passes' gates;
+    its loss and lse equal upipe_loss_fwd's bit for bit (the same statistics
+    epilogue) and its gradients the separate backward's to within the fp16
+    rounding of the logits."""
+    torch = _torch()
+    w = synthetic.LOSS_WORKLOADS[21].with_(L=L, hidden=D, vocab=V, tile_rows=tile)
+    inp = synthetic.make_loss_inputs(w)
+    g = run_fused(inp, tile, dloss)
+    check(g, inp, tile, f"fused loss L={L} D={D} V={V} tile={tile} dloss={dloss}", dloss=dloss)
+    sep = run_gpu(inp, tile, dloss)
+    for k in ("loss", "lse"):
+        assert torch.equal(g[k].view(torch.int32), sep[k].view(torch.int32)), k
+    for k in ("dh", "dw"):
+        e = rel_l2(from_dev_bf16(g[k]), from_dev_bf16(sep[k]))
+        print(f"fused vs separate {k}: rel {e:.2e}", flush=True)
+        assert e <= 5e-3, (k, e)
+
+
+def test_fused_llama3_vocabulary_and_debug_fill():
+    """The Llama-3 vocabulary at hidden 512 (L 192, tiles of 80) against the
+    oracle, and the same outputs bit for bit with the debug NaN fill on."""
+    import headwise_chunked_context_amd as lib
+
+    torch = _torch()
+    w = synthetic.LOSS_WORKLOADS[22].with_(L=192, hidden=512, tile_rows=80)
+    inp = synthetic.make_loss_inputs(w)
+    g = run_fused(inp, 80)
+    check(g, inp, 80, "fused llama3 vocabulary loss L=192 D=512 tile=80")
+    try:
+        lib.debug_enable(True)
+        dbg = run_fused(inp, 80)
+    finally:
+        lib.debug_enable(False)
+    for k in ("loss", "lse"):
+        assert torch.equal(g[k].view(torch.int32), dbg[k].view(torch.int32)), k
+    for k in ("dh", "dw"):
+        assert torch.equal(g[k].view(torch.int16), dbg[k].view(torch.int16)), k

@@ -41,6 +41,10 @@ def test_workspace_holds_no_fp32_logits():
         bwd = up(T * V * 2) + (up(s * T * D * 4) if s > 1 else 0) + up(V * D * 4) + 256
         assert _ws(L, D, V, T, B.PASS_FWD) == (B.UPIPE_OK, fwd), T
         assert _ws(L, D, V, T, B.PASS_BWD) == (B.UPIPE_OK, bwd), T
+        # the fused pass holds both (its [T, V] 2-byte tile serves as fp16
+        # logits, then bf16 dlogits)
+        fused = fwd + bwd
+        assert _ws(L, D, V, T, B.PASS_FWD_BWD) == (B.UPIPE_OK, fused), T
     assert _ws(1000, D, V, 5000, B.PASS_FWD) == _ws(1000, D, V, 1000, B.PASS_FWD)
     # against the whole sequence's fp32 logits (16.8 GB at L 32768): the
     # forward at tile 4096 keeps under 0.1% of that, the backward's bf16 tile
@@ -112,6 +116,32 @@ def test_forward_checks_before_any_gpu_work(kw, code):
 ])
 def test_backward_checks_before_any_gpu_work(kw, code):
     assert _bwd(**kw) == code
+
+
+def _fused(**kw):
+    a = dict(L=1000, D=256, V=1024, T=256, h=P, w=P, t=P, ign=-100, dloss=1.0, loss=P, lse=P, dh=P,
+             dw=P, ws=WS, wsb=1 << 40)
+    a.update(kw)
+    return hc_amd.lib().upipe_loss_fwd_bwd(a["L"], a["D"], a["V"], a["T"], a["h"], a["w"], a["t"],
+                                           a["ign"], a["dloss"], a["loss"], a["lse"], a["dh"],
+                                           a["dw"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=None), B.UPIPE_EINVAL),
+    (dict(loss=None), B.UPIPE_EINVAL),
+    (dict(lse=None), B.UPIPE_EINVAL),
+    (dict(dh=None), B.UPIPE_EINVAL),
+    (dict(dw=None), B.UPIPE_EINVAL),
+    (dict(dh=P + 8), B.UPIPE_EINVAL),
+    (dict(lse=P + 2), B.UPIPE_EINVAL),
+    (dict(wsb=_ws(1000, 256, 1024, 256, B.PASS_BWD)[1]), B.UPIPE_EWORKSPACE),  # backward size
+    (dict(ws=WS + 64), B.UPIPE_EWORKSPACE),
+    (dict(V=1000), B.UPIPE_EUNSUPPORTED),
+    (dict(T=0), B.UPIPE_EINVAL),
+])
+def test_fused_checks_before_any_gpu_work(kw, code):
+    assert _fused(**kw) == code
 
 
 def test_binding_checks_shapes_before_the_library():
