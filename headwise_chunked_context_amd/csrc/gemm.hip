@@ -657,11 +657,17 @@ hipError_t launch_gemm(GemmLayout layout, GemmEpilogue epi, const GemmArgs& a, h
 
 // Split-K factor of a weight-gradient GEMM (reduction over K = L rows).  The
 // 256 x 256 workgroups run one per CU, so with s splits the GEMM takes about
-// ceil(tiles*s / 256) rounds of ceil(L / (64 s)) k steps each, plus a fixed
-// cost per split for its fp32 atomic epilogue, about 5 k steps (fitted to
-// measurements of the layer's shapes).  Each split keeps at least 512 rows.
+// ceil(tiles*s / 256) rounds of ceil(L / (64 s)) k steps each, plus its
+// epilogue over the M x N output: with several splits every split adds its
+// partial tile by fp32 atomics (about 1.2 TB/s, measured), with one split a
+// plain store or read-modify-write (about five times faster).  In units of a
+// round's k step (~2 us at the GEMMs' rate), an atomic pass over M x N
+// elements costs about M N / 600000, a plain one M N / 3000000 (for the
+// attention layer's weight gradients, M N ~ 4-6 million, that is 7-10 k
+// steps per split).  Each split keeps at least 512 rows.
 int gemm_reduction_splits(int64_t L, int M, int N) {
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t elems = (int64_t)M * N;
   int max_s = (int)((L + 511) / 512);
   if (max_s > 32) max_s = 32;
   if (max_s < 1) max_s = 1;
@@ -670,7 +676,8 @@ int gemm_reduction_splits(int64_t L, int M, int N) {
   for (int sp = 1; sp <= max_s; ++sp) {
     const int64_t rounds = (tiles * sp + 255) / 256;
     const int64_t steps = (L + 64LL * sp - 1) / (64LL * sp);
-    const int64_t cost = rounds * steps + 5LL * sp;
+    const int64_t epilogue = sp > 1 ? sp * elems / 600000 : elems / 3000000;
+    const int64_t cost = rounds * steps + epilogue;
     if (cost < best_cost) {
       best_cost = cost;
       best = sp;
