@@ -48,7 +48,7 @@ constexpr int DKDV_THREADS = 512;
 // reach 64 KB.  The workgroup's K and V rows, loaded once, come last.
 struct __attribute__((aligned(16))) DkdvSmem {
   float L0[BMQ], L1[BMQ];           // LSE of the tile's rows (base 2)
-  float E0[BMQ], E1[BMQ];           // D = dO . O of the tile's rows
+  float E0[BMQ], E1[BMQ];           // -D = -(dO . O) of the tile's rows
   uint16_t Q0[BMQ * 128], Q1[BMQ * 128];
   uint16_t O0[BMQ * 128], O1[BMQ * 128];  // dO tiles
   uint16_t K[BNK * 128];
@@ -173,8 +173,16 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
     const int qw0 = q0 + 32 * qh;            // this wave's first query
     if (qw0 + 31 < kw0) return;              // every score is masked
     const bool need_mask = (qw0 < kw0 + 32) || (qw0 + 32 > L);
-    // S = Q K^T and dP = dO V^T: element (query 32*qh + acc_row(r,g), key my_key)
-    f32x16 sv = f32x16{}, dp = f32x16{};
+    // S = Q K^T and dP - D = dO V^T - D: element (query 32*qh +
+    // acc_row(r,g), key my_key); the dP accumulator starts from the tile's
+    // -D rows, so dS below is one multiply per element
+    f32x16 sv = f32x16{}, dp;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(Et + offl + 8 * r4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dp[r4 * 4 + i] = e4[i];
+    }
     // K addresses are rebuilt every step (8 adds) rather than held in 8
     // more registers
     uint32_t kb = lds_addr(Ks) + 2 * dko_init;
@@ -185,10 +193,10 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
       sv = mfma32(*reinterpret_cast<const u32x4*>(Qt + offq[ks]), lds_load16(ka, 0), sv);
       dp = mfma32(*reinterpret_cast<const u32x4*>(Ot + offq[ks]), vreg[ks], dp);
     }
-    // reads two k steps (six reads) ahead, then three per two MFMAs:
-    // measured 0.9% faster than LLVM's generic LDS/MFMA interleave here,
-    // which in turn was 1% faster than the compiler's default order
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    // the -D rows and two k steps (six reads) ahead, then three per two
+    // MFMAs: measured 0.9% faster than LLVM's generic LDS/MFMA interleave
+    // here, which in turn was 1% faster than the compiler's default order
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -206,13 +214,12 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + offl + 8 * r4);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(Et + offl + 8 * r4);
       float pv[4], dsv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = r4 * 4 + i;
         pv[i] = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -l4[i]));
-        dsv[i] = pv[i] * (dp[r] - d4[i]);
+        dsv[i] = pv[i] * dp[r];
       }
       // registers r4*4 .. +3 are B slots 4*(r4%2) .. +3 of step r4/2
       pP[r4 >> 1][2 * (r4 & 1)] = pack_bf16x2(pv[0], pv[1]);

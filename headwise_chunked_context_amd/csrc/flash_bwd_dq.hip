@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
     doreg[ks] = *reinterpret_cast<const u32x4*>(dop + (int64_t)my_q * 128 + ks * 16 + g * 8);
   }
   const float lse2 = a.lse2[(int64_t)head * a.Lp + my_q];
-  const float dval = a.dvec[(int64_t)head * a.Lp + my_q];
+  const float ndval = a.dvec[(int64_t)head * a.Lp + my_q];  // -D
 
   const int kv_end = (q0 + QBM < L) ? q0 + QBM : L;
   const int n_kt = (kv_end + QBN - 1) / QBN;
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], c, -lse2));
-        ds[r] = p * (dp[kb][r] - dval);
+        ds[r] = p * (dp[kb][r] + ndval);
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h)

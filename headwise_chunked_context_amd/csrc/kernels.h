@@ -152,7 +152,7 @@ struct PrepDoutArgs {
   int nh;
   uint16_t* do_rm;         // [nh][Lp][128]
   float* lse2;             // [nh][Lp]
-  float* dvec;             // [nh][Lp]
+  float* dvec;             // [nh][Lp] -D = -(dO . O), negated
   int64_t L, Lp;
 };
 hipError_t launch_prep_dout(const PrepDoutArgs& a, hipStream_t s);
@@ -188,7 +188,7 @@ struct BwdArgs {
   const uint16_t* v;     // [nkv][Lp][128]
   const uint16_t* dO;    // [nh][Lp][128]
   const float* lse2;     // [nh][Lp]
-  const float* dvec;     // [nh][Lp]
+  const float* dvec;     // [nh][Lp] -D (negated: it starts the dP accumulators)
   float* dk_acc;         // [nkv][Lp][128] fp32 cross-chunk accumulators
   float* dv_acc;
   int kv_first, kv_last; // this chunk starts / finishes its KV groups

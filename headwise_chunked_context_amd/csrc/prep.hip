@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void prep_dout_kernel(PrepDoutArgs a) {
     for (int off = 8; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
     *reinterpret_cast<u32x4*>(rm + row * 128 + cc * 8) = v;
     if (cc == 0) {
-      a.dvec[(int64_t)h * a.Lp + row] = dot;
+      a.dvec[(int64_t)h * a.Lp + row] = -dot;  // stored negated: -D
       a.lse2[(int64_t)h * a.Lp + row] = row < a.L ? a.lse[(int64_t)h * a.L + row] * kLog2e : 0.f;
     }
   }
