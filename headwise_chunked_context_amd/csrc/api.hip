@@ -35,6 +35,10 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up64(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
+// Factor the rotated q is stored with: log2(e) / sqrt(d), the softmax scale
+// and the change to base 2, so that q . k is the score in base-2 units
+float q_prescale(int d) { return kLog2e / sqrtf((float)d); }
+
 struct Shape {
   int64_t L, Lp;
   int D, Hq, Hkv, d, hc, G, kc;  // kc = KV heads a chunk touches
@@ -347,6 +351,7 @@ int project_chunk(const Shape& s, const Chunk& ch, const uint16_t* x, const uint
   g.hm_split = s.hc * d;
   g.hm_end = ch.kv_first ? (s.hc + s.kc) * d : s.hc * d;
   g.hm_stride = s.Lp * d;
+  g.hm_q_scale = q_prescale(d);
   // q and k leave the GEMM already rotated: one bf16 rounding after RoPE;
   // v leaves it as fp16 (the forward's P V product takes fp16 operands)
   g.rope_cols = (s.hc + s.kc) * d;
@@ -507,6 +512,7 @@ int attn_fwd_run(const Shape& s, double rope_theta, const uint16_t* x, const uin
     pa.L = s.L;
     pa.Lp = s.Lp;
     pa.rotate = s.proj ? 0 : 1;
+    pa.q_scale = q_prescale(d);
     pa.v_src_f16 = s.proj ? 1 : 0;
     pa.v_out_f16 = 1;
     pa.v_tiles = 1;
@@ -533,7 +539,6 @@ int attn_fwd_run(const Shape& s, double rope_theta, const uint16_t* x, const uin
     fa.lse = lse;
     fa.L = s.L;
     fa.Lp = s.Lp;
-    fa.scale_log2 = kLog2e / sqrtf((float)d);
     UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_FWD, launch_flash_fwd(fa, st));
     if (side) UPIPE_TRY(hipEventRecord(side->done[qslot], st));
   }
@@ -759,6 +764,7 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     pa.L = s.L;
     pa.Lp = s.Lp;
     pa.rotate = s.proj ? 0 : 1;
+    pa.q_scale = q_prescale(d);
     pa.v_src_f16 = s.proj ? 1 : 0;
     pa.v_out_f16 = 0;
     if (!pa.v_only || pa.nkv > 0)
@@ -791,7 +797,6 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       fa.lse = lse2[sl];
       fa.L = s.L;
       fa.Lp = s.Lp;
-      fa.scale_log2 = kLog2e / sqrtf((float)d);
       UPIPE_TRY(timed(UPIPE_KERNEL_ATTN_FWD, sq, [&]() { return launch_flash_fwd(fa, sq); }));
     }
     const uint16_t* o_chunk = recompute ? o_c : o_saved + (int64_t)ch.h0 * d;
@@ -893,8 +898,8 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     ba.kv_head0 = ch.g0;
     ba.L = s.L;
     ba.Lp = s.Lp;
-    ba.scale_log2 = kLog2e / sqrtf((float)d);
     ba.scale = 1.f / sqrtf((float)d);
+    ba.dk_scale = ba.scale / q_prescale(d);
     ba.rope = rope;
     UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_BWD_DKDV, launch_flash_bwd_dkdv(ba, st));
     UPIPE_LAUNCH(UPIPE_KERNEL_ATTN_BWD_DQ, launch_flash_bwd_dq(ba, st));

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
     qreg[ks] = *reinterpret_cast<const u32x4*>(qp + (int64_t)my_q * 128 + ks * 16 + g * 8);
     doreg[ks] = *reinterpret_cast<const u32x4*>(dop + (int64_t)my_q * 128 + ks * 16 + g * 8);
   }
-  const float lse2 = a.lse2[(int64_t)head * a.Lp + my_q];
+  const float nlse2 = a.lse2[(int64_t)head * a.Lp + my_q];  // -LSE, base 2
   const float ndval = a.dvec[(int64_t)head * a.Lp + my_q];  // -D
 
   const int kv_end = (q0 + QBM < L) ? q0 + QBM : L;
@@ -100,7 +100,6 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-  const float c = a.scale_log2;
 
   auto step = [&](int kt, const uint16_t* Kt, const uint16_t* Vt) {
     const int kstart = kt * QBN;
@@ -134,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], c, -lse2));
+        const float p = __builtin_amdgcn_exp2f(sv[kb][r] + nlse2);
         ds[r] = p * (dp[kb][r] + ndval);
       }
 #pragma unroll

@@ -28,9 +28,10 @@
 //    output inside its error budget where bf16's 7 bits do not.  The row
 //    sum is taken from the same fp16 P by v_dot2_f32_f16, so numerator and
 //    denominator see identical probabilities;
-//  * the softmax runs in base 2 with the 1/sqrt(d) scale folded into one FMA;
-//    the running maximum is raised lazily (only when a score exceeds it by
-//    more than 2^8), which removes the per-tile rescale of O;
+//  * the softmax runs in base 2: q arrives multiplied by log2(e)/sqrt(d), so
+//    the score MFMAs produce base-2 exponents directly; the running maximum
+//    is raised lazily (only when a score exceeds it by more than 2^8), which
+//    removes the per-tile rescale of O;
 //  * the two LDS buffers are distinct arrays and the key loop is unrolled
 //    by two, so every LDS address is a per-lane base plus an immediate and
 //    the compiler can see that reads of one buffer never alias the copy in
@@ -112,9 +113,8 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   f32x16 acc_o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
-  float m_run = -__builtin_inff();
+  float m_run = -__builtin_inff();  // base-2 units, as the scores
   float l_run = 0.f;
-  const float c = a.scale_log2;
   const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 
   // S^T of one key tile: element (key kb*32 + acc_row(r,g), query my_q)
@@ -157,15 +157,15 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[1][r]), sc[1][r + 1]);
     mx = half_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx * c > fmaf(m_run, c, 8.f))) {
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc_o[db] *= alpha;
       m_run = m_new;
     }
-    const float mc = m_run * c;
+    const float mc = m_run;
     // scores of the next tile (unused past the last tile or the diagonal;
     // the buffer then holds stale but finite-or-ignored data)
     f32x16 sn[2];
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       float pr[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -mc));
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(sc[kb][r] - mc);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
                  pack_bf16x2(acc_o[db][4 * j + 2] * inv, acc_o[db][4 * j + 3] * inv)};
       *reinterpret_cast<u32x2*>(orow + d) = w;
     }
-  if (g == 0) a.lse[(int64_t)hg * a.L + my_q] = (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  if (g == 0) a.lse[(int64_t)hg * a.L + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 }  // namespace

@@ -537,6 +537,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
           lo = f32x4{v[0], v[1], v[2], v[3]};
           hi = f32x4{v[4], v[5], v[6], v[7]};
         }
+        if (EPI == EPI_STORE_BF16 && head_major && n < p.hm_split) {
+          lo *= p.hm_q_scale;
+          hi *= p.hm_q_scale;
+        }
         if (EPI == EPI_ACCUM_BF16) {
           const u32x4 o = old[it];
           lo[0] += bf16_lo(o[0]); lo[1] += bf16_hi(o[0]);

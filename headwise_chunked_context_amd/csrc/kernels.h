@@ -76,6 +76,9 @@ struct GemmArgs {
   uint16_t* hm_k;
   int hm_split, hm_end;
   int64_t hm_stride;
+  // factor applied to the hm_q columns after RoPE, before the rounding
+  // (the attention kernels take q pre-multiplied by log2(e) / sqrt(d))
+  float hm_q_scale;
   // NT only, if > 0: rows of A that exist (reads of later rows clamp to the
   // last one) and rows of C that are stored; M may then exceed it, for the
   // head-major columns' padding rows
@@ -138,11 +141,13 @@ struct PrepArgs {
   int v_tiles;             // write v (fp16) as the forward's transposed
                            // 64-key tiles instead of row-major (see prep.hip)
   int v_only;              // only the v heads (the q and k heads are skipped)
+  float q_scale;           // q heads are multiplied by this (after RoPE) before rounding
 };
 hipError_t launch_prep_qkv(const PrepArgs& a, const RopeTable& t, hipStream_t s);
 
 // dO prep for the backward: head-major dO, D_i = dO_i . O_i and the base-2
-// log-sum-exp of each row, all padded to Lp.
+// log-sum-exp of each row, all padded to Lp; D and the log-sum-exp are
+// stored negated (they start the backward kernels' accumulators).
 struct PrepDoutArgs {
   const uint16_t* src_do;  // head j at src_do + j*128, row stride do_ld
   int64_t do_ld;
@@ -151,7 +156,7 @@ struct PrepDoutArgs {
   const float* lse;        // head j at lse + j*L
   int nh;
   uint16_t* do_rm;         // [nh][Lp][128]
-  float* lse2;             // [nh][Lp]
+  float* lse2;             // [nh][Lp] -LSE in base 2, negated
   float* dvec;             // [nh][Lp] -D = -(dO . O), negated
   int64_t L, Lp;
 };
@@ -165,8 +170,11 @@ hipError_t launch_fill(void* p, size_t bytes, uint32_t pattern, hipStream_t s);
 extern bool g_debug_fill;
 
 // ---------------------------------------------------------- attention
+// q arrives rotated and pre-multiplied by log2(e) / sqrt(d) (by the
+// projection GEMM's epilogue or by prep_qkv), so q . k is the score in
+// base-2 units and the softmax needs no scaling.
 struct FwdArgs {
-  const uint16_t* q;    // [nh][Lp][128], rotated
+  const uint16_t* q;    // [nh][Lp][128], rotated, times log2(e)/sqrt(d)
   const uint16_t* k;    // [nkv][Lp][128], rotated
   const uint16_t* v;    // [nkv][Lp/64] transposed fp16 tiles of 128 x 64 (prep.hip)
   int nh;               // query heads in this chunk
@@ -178,16 +186,15 @@ struct FwdArgs {
   int64_t o_ld;
   float* lse;           // [.][L]; q head h at row h - o_head0
   int64_t L, Lp;
-  float scale_log2;     // log2(e) / sqrt(d)
 };
 hipError_t launch_flash_fwd(const FwdArgs& a, hipStream_t s);
 
 struct BwdArgs {
-  const uint16_t* q;     // [nh][Lp][128] rotated
+  const uint16_t* q;     // [nh][Lp][128] rotated, times log2(e)/sqrt(d) (as FwdArgs)
   const uint16_t* k;     // [nkv][Lp][128] rotated
   const uint16_t* v;     // [nkv][Lp][128]
   const uint16_t* dO;    // [nh][Lp][128]
-  const float* lse2;     // [nh][Lp]
+  const float* lse2;     // [nh][Lp] -LSE in base 2 (negated: it starts the S accumulators)
   const float* dvec;     // [nh][Lp] -D (negated: it starts the dP accumulators)
   float* dk_acc;         // [nkv][Lp][128] fp32 cross-chunk accumulators
   float* dv_acc;
@@ -200,8 +207,8 @@ struct BwdArgs {
   int group;             // G
   int q_head0, kv_head0; // global indices (q head h uses kv head h / G)
   int64_t L, Lp;
-  float scale_log2;      // log2(e)/sqrt(d)
-  float scale;           // 1/sqrt(d)
+  float dk_scale;        // dK = dk_scale * dS^T q: 1/sqrt(d) over q's factor
+  float scale;           // 1/sqrt(d) (dQ = scale * dS K)
   RopeTable rope;
 };
 // dK, dV of the chunk's KV heads (key-stationary) ...

@@ -15,15 +15,23 @@ namespace {
 constexpr int ROWS = 64;
 
 // rotate 8 consecutive elements (4 pairs starting at pair p0) of one row
-__device__ __forceinline__ u32x4 rotate8(u32x4 v, const RopeTable& t, int64_t pos, int p0) {
+// and multiply them by mul, in fp32 before the one rounding
+__device__ __forceinline__ u32x4 rotate8(u32x4 v, const RopeTable& t, int64_t pos, int p0, float mul) {
   u32x4 out;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float c, s;
     rope_cos_sin(t, pos, p0 + j, c, s);
     float e = bf16_lo(v[j]), o = bf16_hi(v[j]);
-    out[j] = pack_bf16x2(e * c - o * s, e * s + o * c);
+    out[j] = pack_bf16x2((e * c - o * s) * mul, (e * s + o * c) * mul);
   }
+  return out;
+}
+// multiply 8 bf16 elements by mul
+__device__ __forceinline__ u32x4 scale8(u32x4 v, float mul) {
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = pack_bf16x2(bf16_lo(v[j]) * mul, bf16_hi(v[j]) * mul);
   return out;
 }
 
@@ -78,8 +86,9 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a, RopeTable t) 
   const int64_t r0 = (int64_t)blockIdx.x * ROWS;
   const uint16_t* src;
   uint16_t* dst;
-  bool rot = a.rotate != 0, is_v = false;
+  bool rot = a.rotate != 0, is_v = false, is_q = false;
   if (slot < a.nq) {
+    is_q = true;
     src = a.src_q + slot * 128;
     dst = a.q_rm + (int64_t)slot * a.Lp * 128;
   } else if (slot < a.nq + a.nkv) {
@@ -106,7 +115,10 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a, RopeTable t) 
     u32x4 v = {0, 0, 0, 0};
     if (row < a.L) {
       v = *reinterpret_cast<const u32x4*>(src + row * a.src_ld + cc * 8);
-      if (rot) v = rotate8(v, t, row, cc * 4);
+      if (rot)
+        v = rotate8(v, t, row, cc * 4, is_q ? a.q_scale : 1.f);
+      else if (is_q)
+        v = scale8(v, a.q_scale);
       if (is_v && a.v_src_f16 && !a.v_out_f16) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(f16_lo(v[j]), f16_hi(v[j]));
@@ -145,7 +157,7 @@ __global__ __launch_bounds__(256) void prep_dout_kernel(PrepDoutArgs a) {
     *reinterpret_cast<u32x4*>(rm + row * 128 + cc * 8) = v;
     if (cc == 0) {
       a.dvec[(int64_t)h * a.Lp + row] = -dot;  // stored negated: -D
-      a.lse2[(int64_t)h * a.Lp + row] = row < a.L ? a.lse[(int64_t)h * a.L + row] * kLog2e : 0.f;
+      a.lse2[(int64_t)h * a.Lp + row] = row < a.L ? -a.lse[(int64_t)h * a.L + row] * kLog2e : 0.f;
     }
   }
 }

@@ -68,7 +68,9 @@
  * Precision
  * ---------
  *  - The projections and the score product Q K^T take bf16 operands with
- *    fp32 accumulation; the rotated q and k are held in bf16.
+ *    fp32 accumulation; the rotated q and k are held in bf16 (q multiplied
+ *    by log2(e)/sqrt(head_dim) in fp32 first, so that the scores come out
+ *    as base-2 exponents; the relative rounding is unchanged).
  *  - The forward's O = P V product takes fp16 operands (P in [0, 256], v
  *    converted from bf16 to fp16) with fp32 accumulation: fp16's 10-bit
  *    mantissa keeps O inside its error budget where bf16's 7 bits do not.

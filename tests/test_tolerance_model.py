@@ -3,8 +3,9 @@
 The saved O and the LSE are gated more loosely than the layer output
 (O: max-abs <= 2e-2 max(1, max|O|); LSE: 2e-2 + 2e-3 |LSE|).  This test shows
 that rounding alone reaches those sizes: the oracle's own per-head routines
-are evaluated on the operands the HIP path stores - the rotated q and k
-rounded to bf16, v rounded to fp16 (the forward's P V operand), all from
+are evaluated on the operands the HIP path stores - the rotated q (times
+log2(e)/sqrt(d), the factor it is stored with) and k rounded to bf16, v
+rounded to fp16 (the forward's P V operand), all from
 bf16-rounded projections - and the result O rounded to bf16, with every
 other step exact in fp64.  Nothing of the HIP path is used; only where the
 roundings sit is taken from its storage formats.
@@ -28,6 +29,13 @@ def _f16(a):
     return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
+def _q_stored(q_rot, d):
+    """The rotated q as held: times log2(e)/sqrt(d) in fp32, rounded to bf16
+    (returned with the factor divided out again)."""
+    c = np.float32(np.float32(1.4426950408889634) / np.sqrt(np.float32(d)))
+    return _bf16(np.asarray(q_rot, dtype=np.float32) * c) / np.float64(c)
+
+
 def _model_o_lse(w, inp, n_heads):
     """O and LSE of the first n_heads q heads with the storage roundings."""
     d, G = w.head_dim, w.n_q // w.n_kv
@@ -46,7 +54,7 @@ def _model_o_lse(w, inp, n_heads):
             v = _f16(_bf16(x @ wq[vr:vr + d].T))
             kv = {g: (k, v)}
         k, v = kv[g]
-        q = _bf16(rope(x @ wq[h * d:(h + 1) * d].T, pos, w.theta))
+        q = _q_stored(rope(x @ wq[h * d:(h + 1) * d].T, pos, w.theta), d)
         oh, lh = attention_fwd_head(q, k, v)
         o[:, h * d:(h + 1) * d] = _bf16(oh)
         lse[h] = lh
