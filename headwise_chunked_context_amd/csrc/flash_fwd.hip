@@ -47,6 +47,15 @@ namespace {
 constexpr int BM = 128;       // queries per workgroup
 constexpr int BN = 64;        // keys per step
 
+// max(x, x of lane ^ 32) by the lane-swap VALU instruction (no LDS round
+// trip): one copy of x gets its upper half from the other's lower half and
+// vice versa, so the two results hold the two halves in either order
+__device__ __forceinline__ float half_max_swap(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+}
+
 __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t K0[BN * 128];
   __shared__ __attribute__((aligned(16))) uint16_t K1[BN * 128];
@@ -156,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[0][r]), sc[0][r + 1]);
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[1][r]), sc[1][r + 1]);
-    mx = half_max(mx);
+    mx = half_max_swap(mx);
     if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -203,6 +212,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     }
     l_run += ls0 + ls1;
     __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     // O^T += V^T P^T; B slot t of step st is key 16*st + 8*(t/4) + 4*g + t%4,
     // the order in which the V^T tile stores the keys of each 16-key step
 #pragma unroll
@@ -210,6 +220,14 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
         acc_o[db] = mfma32_f16(*reinterpret_cast<const u32x4*>(Vc + voff[st] + db * 2048), pb[st], acc_o[db]);
+    // V^T reads kept four MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     sc[0] = sn[0];
     sc[1] = sn[1];
   };
