@@ -32,7 +32,9 @@
  * is ignored the loss is 0 and so are the gradients (a mean over no terms
  * taken as 0); a target outside [0, vocab) that is not ignore_index makes
  * its row's loss, the mean and that row's gradients NaN (and, through the
- * sum, dW); tiles are consecutive rows, the last one ragged.
+ * sum, dW); tiles are consecutive rows, the last one ragged.  Inputs are
+ * expected finite: a NaN or Inf in h or W gives unspecified (possibly
+ * finite) results, since the row maxima are taken without NaN handling.
  *
  * Argument rules
  * --------------

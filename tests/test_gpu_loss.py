@@ -126,15 +126,18 @@ def test_tile_invariance_and_reproducibility():
         assert e <= 1e-3, (tile, e)
 
 
-def test_ignored_rows_and_out_of_range_targets():
+@pytest.mark.parametrize("fused", [False, True])
+def test_ignored_rows_and_out_of_range_targets(fused):
     """Every row ignored: loss 0, gradients 0.  One target equal to the
     vocabulary size: the loss and that row's dh are NaN, the other rows of
-    dh match the oracle."""
+    dh match the oracle.  The same for the separate passes and the fused
+    forward-backward."""
     torch = _torch()
+    run = run_fused if fused else run_gpu
     w = synthetic.LOSS_WORKLOADS[21].with_(L=200)
     inp = synthetic.make_loss_inputs(w)
     none = dict(inp, targets=np.full(200, IGN, dtype=np.int32))
-    g = run_gpu(none, 64)
+    g = run(none, 64)
     assert float(from_dev_f32(g["loss"])[0]) == 0.0
     assert not torch.any(g["dh"].float() != 0) and not torch.any(g["dw"].float() != 0)
     assert np.isfinite(from_dev_f32(g["lse"])).all()
@@ -142,7 +145,7 @@ def test_ignored_rows_and_out_of_range_targets():
     bad = inp["targets"].copy()
     r = int(np.nonzero(bad != IGN)[0][5])
     bad[r] = w.vocab
-    g = run_gpu(dict(inp, targets=bad), 64)
+    g = run(dict(inp, targets=bad), 64)
     assert np.isnan(float(from_dev_f32(g["loss"])[0]))
     gdh = from_dev_bf16(g["dh"])
     assert np.isnan(gdh[r]).all()
