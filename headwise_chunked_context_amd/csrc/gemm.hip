@@ -107,6 +107,27 @@ __device__ __forceinline__ int64_t seg_map(const RowSegments& s, int idx) {
   return s.row0[0] + idx;  // unreachable for valid maps
 }
 
+// Maximum and sum over the 32 lanes of each half-wave by VALU lane exchanges
+// (DPP within 4, 8 and 16 lanes, then the swap of 16-lane rows) instead of
+// LDS permutes with their round trips.  Every lane ends with the same value
+// (each step combines two equal-sized partial results; fp addition is
+// commutative), so the result is reproducible.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <bool MAX>
+__device__ __forceinline__ float half_wave_reduce(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  x = op(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]: lane ^ 1
+  x = op(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]: lane ^ 2
+  x = op(x, dpp_mov<0x141>(x));  // row_half_mirror: the other quad of 8 lanes
+  x = op(x, dpp_mov<0x140>(x));  // row_mirror: the other 8 of 16 lanes
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 0<->1, 2<->3
+  return op(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+}
+
 // s_waitcnt vmcnt(n), other counters untouched
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -461,15 +482,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
           y[i] = row_ok && n + i < p.N ? src[i] * kLog2e : -__builtin_inff();
           mx = fmaxf(mx, y[i]);
         }
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        mx = half_wave_reduce<true>(mx);
         float sum = 0.f;
         if (mx != -__builtin_inff()) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) sum += __builtin_amdgcn_exp2f(y[i] - mx);
         }
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+        sum = half_wave_reduce<false>(sum);
         if (row_ok) {
           if (cc == 0) {
             const int nct = (p.N + BN - 1) / BN;
