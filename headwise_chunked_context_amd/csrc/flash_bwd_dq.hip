@@ -58,6 +58,12 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
   }
   const float nlse2 = a.lse2[(int64_t)head * a.Lp + my_q];  // -LSE, base 2
   const float ndval = a.dvec[(int64_t)head * a.Lp + my_q];  // -D
+  // the lane's -D in all 16 registers: the starting value of each dP^T
+  // chain (the first MFMA reads it as its C operand), so dP - D costs no
+  // vector instruction per element
+  f32x16 nd16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nd16[r] = ndval;
 
   const int kv_end = (q0 + QBM < L) ? q0 + QBM : L;
   const int n_kt = (kv_end + QBN - 1) / QBN;
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sv[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      dp[kb] = nd16;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         sv[kb] = mfma32(*reinterpret_cast<const u32x4*>(Kt + koff[ks] + kb * 4096), qreg[ks], sv[kb]);
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(sv[kb][r] + nlse2);
-        ds[r] = p * (dp[kb][r] + ndval);
+        ds[r] = p * dp[kb][r];
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h)
