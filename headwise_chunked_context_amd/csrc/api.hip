@@ -770,9 +770,9 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
     if (!pa.v_only || pa.nkv > 0)
       UPIPE_TRY(timed(UPIPE_KERNEL_PREP, sq, [&]() { return launch_prep_qkv(pa, rope, sq); }));
 
-    // 1b. full recompute: the forward's attention of the chunk's heads again,
-    // from the same q, k and (fp16 tile) v, into o_c; it equals the
-    // forward's O bit for bit.  Its LSE output is scratch in lse2.
+    // 1b. full recompute: the chunk's attention output again, into o_c, in
+    // one pass from the same q, k and (fp16 tile) v and the saved LSE
+    // (P = exp(S - LSE) is final at once: no running maximum or row sum)
     if (recompute) {
       if (ch.kv_first) {
         PrepArgs pv = pa;
@@ -794,10 +794,11 @@ int upipe_attn_bwd(int64_t seq_len, int32_t hidden, int32_t n_q_heads, int32_t n
       fa.o_head0 = ch.h0;
       fa.o = o_c;
       fa.o_ld = (int64_t)s.hc * d;
-      fa.lse = lse2[sl];
+      fa.lse = nullptr;  // not written from the LSE
+      fa.lse_in = lse;
       fa.L = s.L;
       fa.Lp = s.Lp;
-      UPIPE_TRY(timed(UPIPE_KERNEL_ATTN_FWD, sq, [&]() { return launch_flash_fwd(fa, sq); }));
+      UPIPE_TRY(timed(UPIPE_KERNEL_ATTN_FWD, sq, [&]() { return launch_flash_fwd_lse(fa, sq); }));
     }
     const uint16_t* o_chunk = recompute ? o_c : o_saved + (int64_t)ch.h0 * d;
     const int64_t o_chunk_ld = recompute ? (int64_t)s.hc * d : (int64_t)s.Hq * d;

@@ -56,6 +56,11 @@ __device__ __forceinline__ float half_max_swap(float x) {
   return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
 }
 
+// FROM_LSE: the backward's recompute of O from the forward's saved LSE.  The
+// probabilities P = exp2(s - LSE2) are final at once, so the running
+// maximum, its rescale and the row sum drop out and O needs no division;
+// nothing but O is written.
+template <bool FROM_LSE>
 __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t K0[BN * 128];
   __shared__ __attribute__((aligned(16))) uint16_t K1[BN * 128];
@@ -122,7 +127,10 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   f32x16 acc_o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
-  float m_run = -__builtin_inff();  // base-2 units, as the scores
+  // the running maximum in base-2 units, as the scores; from the saved LSE
+  // (base 2) when it is given (padding rows: 0, their O is not stored)
+  float m_run = -__builtin_inff();
+  if (FROM_LSE) m_run = my_q < L ? a.lse_in[(int64_t)(a.q_head0 + head) * L + my_q] * kLog2e : 0.f;
   float l_run = 0.f;
   const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 
@@ -160,19 +168,21 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     // exceeds it by more than 2^8 in the exponent (wave-uniform), so the
     // 64-register rescale of O runs a few times per row instead of every
     // tile; in between P <= 256, well inside fp16 and fp32
-    float mx = fmaxf(sc[0][0], sc[0][1]);
+    if constexpr (!FROM_LSE) {
+      float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[0][r]), sc[0][r + 1]);
+      for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[0][r]), sc[0][r + 1]);
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[1][r]), sc[1][r + 1]);
-    mx = half_max_swap(mx);
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[1][r]), sc[1][r + 1]);
+      mx = half_max_swap(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc_o[db] *= alpha;
-      m_run = m_new;
+        for (int db = 0; db < 4; ++db) acc_o[db] *= alpha;
+        m_run = m_new;
+      }
     }
     const float mc = m_run;
     // scores of the next tile (unused past the last tile or the diagonal;
@@ -203,7 +213,9 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
         for (int t = 0; t < 4; ++t) {
           const f32x2 pair = {pr[8 * h + 2 * t], pr[8 * h + 2 * t + 1]};
           const f16x2 hp = __builtin_convertvector(pair, f16x2);
-          if (t & 1)
+          if (FROM_LSE)
+            ;  // no row sum: P is already normalised
+          else if (t & 1)
             ls1 = __builtin_amdgcn_fdot2(hp, ones, ls1, false);
           else
             ls0 = __builtin_amdgcn_fdot2(hp, ones, ls0, false);
@@ -255,9 +267,9 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     __syncthreads();
   }
 
-  const float l_tot = half_sum(l_run);
+  const float l_tot = FROM_LSE ? 1.f : half_sum(l_run);
   if (my_q >= L) return;
-  const float inv = 1.f / l_tot;
+  const float inv = FROM_LSE ? 1.f : 1.f / l_tot;  // (with the LSE, P sums to 1)
   const int hg = a.q_head0 - a.o_head0 + head;
   uint16_t* orow = a.o + (int64_t)my_q * a.o_ld + (int64_t)hg * 128;
 #pragma unroll
@@ -269,14 +281,21 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
                  pack_bf16x2(acc_o[db][4 * j + 2] * inv, acc_o[db][4 * j + 3] * inv)};
       *reinterpret_cast<u32x2*>(orow + d) = w;
     }
-  if (g == 0) a.lse[(int64_t)hg * a.L + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  if (!FROM_LSE && g == 0)
+    a.lse[(int64_t)hg * a.L + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 }  // namespace
 
 hipError_t launch_flash_fwd(const FwdArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.Lp / BM) * a.nh));
-  hipLaunchKernelGGL(flash_fwd_kernel, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(flash_fwd_kernel<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flash_fwd_lse(const FwdArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.Lp / BM) * a.nh));
+  hipLaunchKernelGGL(flash_fwd_kernel<true>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

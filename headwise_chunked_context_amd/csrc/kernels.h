@@ -186,8 +186,12 @@ struct FwdArgs {
   int64_t o_ld;
   float* lse;           // [.][L]; q head h at row h - o_head0
   int64_t L, Lp;
+  const float* lse_in;  // launch_flash_fwd_lse: [Hq][L] saved LSE (natural log),
+                        // q head h at row h; lse is not written then
 };
 hipError_t launch_flash_fwd(const FwdArgs& a, hipStream_t s);
+// O only, from the forward's saved LSE (the backward's full recompute)
+hipError_t launch_flash_fwd_lse(const FwdArgs& a, hipStream_t s);
 
 struct BwdArgs {
   const uint16_t* q;     // [nh][Lp][128] rotated, times log2(e)/sqrt(d) (as FwdArgs)

@@ -203,18 +203,23 @@ int upipe_attn_fwd_static(int64_t seq_len, int32_t hidden, int32_t n_q_heads,
  *  o_saved, lse    the forward's outputs for the same inputs.  In projection
  *           mode o_saved may be NULL ("full recompute"): each chunk's
  *           attention output is then recomputed from the recomputed q/k/v
- *           (4*head_dim FLOPs more per causal pair and q head) into
- *           per-chunk workspace, so nothing of size L*Hq*head_dim has to
- *           outlive the forward: activation checkpointing, one step of the
- *           memory progression in "Untied Ulysses Pushes Llama-3-8B Training
- *           to 5 Million Tokens", applied to this layer's own saved output.
- *           Needs the UPIPE_PASS_BWD_RECOMPUTE workspace.  dx equals that
- *           of the o_saved call bit for bit.  dw_qkv and dw_o do too when
- *           the weight-gradient GEMMs split their reduction over L in at
- *           most two parts (short L); with more parts the parts meet by
- *           fp32 atomic adds in an order that varies from run to run, so
- *           a few bf16 values may differ by one unit in the last place
- *           between any two calls, with or without o_saved.
+ *           and the saved lse, in one pass (P = exp(S - lse) needs no
+ *           running maximum or row sum; 4*head_dim FLOPs more per causal
+ *           pair and q head), into per-chunk workspace, so nothing of size
+ *           L*Hq*head_dim has to outlive the forward: activation
+ *           checkpointing, one step of the memory progression in "Untied
+ *           Ulysses Pushes Llama-3-8B Training to 5 Million Tokens", applied
+ *           to this layer's own saved output.  Needs the
+ *           UPIPE_PASS_BWD_RECOMPUTE workspace.  The recomputed O differs
+ *           from the forward's by rounding (it is normalised by the saved
+ *           lse instead of its own row sum), so the gradients match those
+ *           of the o_saved call to about 2e-3 relative, not bit for bit.
+ *           With o_saved, dx is bitwise reproducible from run to run;
+ *           dw_qkv and dw_o are too when the weight-gradient GEMMs split
+ *           their reduction over L in at most two parts (short L); with
+ *           more parts the parts meet by fp32 atomic adds in an order that
+ *           varies from run to run, so a few bf16 values may differ by one
+ *           unit in the last place between any two calls.
  *  dy       [L, hidden] bf16 upstream gradient of y, or dO [L, Hq*head_dim]
  *  dx       [L, hidden] bf16 out, or dqkv [L, (Hq+2Hkv)*head_dim] (hidden == 0)
  *  dw_qkv   [(Hq+2Hkv)*head_dim, hidden] bf16 out, NULL iff hidden == 0

@@ -174,12 +174,13 @@ def test_qwen32b_share_full_length_chunk_sweep():
 
 def test_llama8b_layer_recompute_and_pipeline_modes():
     """The benchmarked layer in the optional modes.  The pipelined forward
-    gives the one-stream forward's bits.  The recompute and the pipelined
-    backward give the saved-output backward's dx bits; weight gradients are summed by
-    split-K fp32 atomics in an order that varies from run to run, which moves
-    a few bf16 values by one unit in the last place (2^-8 relative): they are
-    held to 99.9% identical values and the relative L2 that a one-ulp change
-    of 0.1% of them gives (sqrt(1e-3) * 2^-8 ~ 1.2e-4, bound 2e-4)."""
+    gives the one-stream forward's bits.  The pipelined backward gives the
+    saved-output backward's dx bits; weight gradients are summed by split-K
+    fp32 atomics in an order that varies from run to run, which moves a few
+    bf16 values by one unit in the last place (2^-8 relative): they are held
+    to 99.9% identical values and the relative L2 that a one-ulp change of
+    0.1% of them gives (sqrt(1e-3) * 2^-8 ~ 1.2e-4, bound 2e-4).  The
+    recompute backward's gradients are within 5e-3 relative L2."""
     import torch
 
     import headwise_chunked_context_amd as lib
@@ -212,11 +213,18 @@ def test_llama8b_layer_recompute_and_pipeline_modes():
     finally:
         lib.pipeline_enable(False)
     torch.cuda.synchronize()
-    for mode, res in (("recompute", rec), ("pipelined", pip)):
-        assert torch.equal(bits(ref[0]), bits(res[0])), (mode, "dx")
-        for name, a, b in zip(("dw_qkv", "dw_o"), ref[1:], res[1:]):
-            af, bf = a.float(), b.float()
-            rel = float(torch.linalg.vector_norm(af - bf) / torch.linalg.vector_norm(af))
-            same = float((bits(a) == bits(b)).float().mean())
-            print(f"{w.name}: {mode} backward {name} rel-L2 {rel:.2e}, identical {same:.6f}", flush=True)
-            assert rel <= 2e-4 and same >= 0.999, (mode, name)
+    assert torch.equal(bits(ref[0]), bits(pip[0])), ("pipelined", "dx")
+    for name, a, b in zip(("dw_qkv", "dw_o"), ref[1:], pip[1:]):
+        af, bf = a.float(), b.float()
+        rel = float(torch.linalg.vector_norm(af - bf) / torch.linalg.vector_norm(af))
+        same = float((bits(a) == bits(b)).float().mean())
+        print(f"{w.name}: pipelined backward {name} rel-L2 {rel:.2e}, identical {same:.6f}", flush=True)
+        assert rel <= 2e-4 and same >= 0.999, ("pipelined", name)
+    # the recompute normalises the recomputed O by the saved LSE, not by its
+    # own row sum: its gradients match the saved-output backward's to the
+    # rounding of O
+    for name, a, b in zip(("dx", "dw_qkv", "dw_o"), ref, rec):
+        af, bf = a.float(), b.float()
+        rel = float(torch.linalg.vector_norm(af - bf) / torch.linalg.vector_norm(af))
+        print(f"{w.name}: recompute backward {name} rel-L2 {rel:.2e}", flush=True)
+        assert rel <= 5e-3, ("recompute", name)
