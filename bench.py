@@ -30,7 +30,8 @@ layer shape at a short sequence), reported in the same unit.
 
 workloads: every other layer shape the metric is quoted on, each timed the
 same way for a few steps on inputs drawn on the device (same distributions as
-the seeded host recipe): the small GQA layer, the two one-GPU shares of the
+the seeded host recipe): the small GQA layer (also as a HIP
+graph replay of its recorded step, where it is launch-bound), the two one-GPU shares of the
 Llama-3-8B model (q/k/v given, L 524288 and 1048576), the 32B-class share
 at every head chunk of its sweep (with and without the two-slot pipeline),
 and the benchmarked layer with the full-recompute backward and with the
@@ -324,6 +325,39 @@ def time_layer(lib, w, x, wq, wo, dy, steps, warmup, recompute=False):
                 bwd_pass=bwd_pass)
 
 
+def time_layer_graph(lib, w, x, wq, wo, dy, steps, warmup):
+    """The step of time_layer recorded once into a HIP graph (torch's
+    CUDAGraph on its capture stream; every entry point enqueues kernel
+    launches only), then replayed: `warmup` untimed replays, then `steps`
+    timed ones.  Returns the workspace sizes and ms per step."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    hc = w.head_chunk
+    ws_f = lib.workspace_bytes(w.L, w.hidden, w.n_q, w.n_kv, w.head_dim, hc, lib.PASS_FWD)
+    ws_b = lib.workspace_bytes(w.L, w.hidden, w.n_q, w.n_kv, w.head_dim, hc, lib.PASS_BWD)
+    ws = torch.empty(max(ws_f, ws_b), dtype=torch.uint8, device=dev)
+
+    def step():
+        _, o, lse = lib.attn_fwd(x, wq, wo, w.n_q, w.n_kv, hc, w.theta, workspace=ws)
+        lib.attn_bwd(x, wq, wo, o, lse, dy, w.n_q, w.n_kv, hc, w.theta, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return dict(ms=(t1 - t0) * 1e3 / steps, ws_f=ws_f, ws_b=ws_b)
+
+
 def sweep(lib) -> dict:
     """Every other workload, a few steps each (inputs drawn on the device)."""
     import torch
@@ -331,7 +365,7 @@ def sweep(lib) -> dict:
     import synthetic
 
     W = synthetic.WORKLOADS
-    plan = [(W[1], 3, 10, False), (W[3], 1, 2, False), (W[5], 1, 1, False)]
+    plan = [(W[1], 3, 10, False), (W[1], 3, 10, "graph"), (W[3], 1, 2, False), (W[5], 1, 1, False)]
     # the benchmarked layer in its optional modes: full recompute (o_saved
     # NULL) and the two-slot pipeline
     plan += [(W[2], 1, 3, "recompute"), (W[2], 1, 3, True)]
@@ -340,12 +374,14 @@ def sweep(lib) -> dict:
     plan += [(W[4].with_(head_chunk=c), 1, 2, pipe) for pipe in (False, True) for c in (1, 2, 4, 8)]
     out = {}
     for w, warmup, steps, mode in plan:
-        pipe, recompute = mode is True, mode == "recompute"
+        pipe, recompute, graph = mode is True, mode == "recompute", mode == "graph"
         key = w.name if w.wid != 4 else f"{w.name}_chunk{w.head_chunk}"
         if pipe:
             key += "_pipelined"
         if recompute:
             key += "_recompute"
+        if graph:
+            key += "_graph"
         torch.cuda.empty_cache()
         x, wq, wo, dy = device_inputs(w, seed=1000 * w.wid)
         torch.cuda.synchronize()
@@ -353,7 +389,10 @@ def sweep(lib) -> dict:
         torch.cuda.reset_peak_memory_stats()   # the layer's own peak, not the draw's
         lib.pipeline_enable(pipe)
         try:
-            r = time_layer(lib, w, x, wq, wo, dy, steps, warmup, recompute=recompute)
+            if graph:
+                r = time_layer_graph(lib, w, x, wq, wo, dy, steps, warmup)
+            else:
+                r = time_layer(lib, w, x, wq, wo, dy, steps, warmup, recompute=recompute)
         finally:
             lib.pipeline_enable(False)
         peak = torch.cuda.max_memory_allocated()
@@ -364,15 +403,16 @@ def sweep(lib) -> dict:
             "seq_len": w.L, "hidden": w.hidden, "n_q_heads": w.n_q, "n_kv_heads": w.n_kv,
             "head_chunk": w.head_chunk, "pipeline": pipe,
             "backward": "recompute attention output" if recompute else "saved attention output",
+            "launch": "hip graph replay" if graph else "eager",
             "steps": steps, "warmup": warmup,
             "ms_per_step": round(r["ms"], 3),
             "tflops": round(flops / (r["ms"] * 1e-3) / 1e12, 2),
-            "roofline_kernel": r["dom"],
-            "roofline_frac": round(r["achieved"] / PEAK_BF16_TFLOPS, 4),
+            "roofline_kernel": r.get("dom"),
+            "roofline_frac": round(r["achieved"] / PEAK_BF16_TFLOPS, 4) if "achieved" in r else None,
             "workspace_gib": {"fwd": round(r["ws_f"] / 2**30, 4), "bwd": round(r["ws_b"] / 2**30, 4)},
             "peak_allocated_gib": round(peak / 2**30, 3),
             "peak_allocated_minus_inputs_gib": round((peak - io) / 2**30, 3),
-            "hbm_passes": r["hbm"],
+            "hbm_passes": r.get("hbm"),
         }
         print(f"bench: {key}: {out[key]['ms_per_step']} ms/step, {out[key]['tflops']} TFLOP/s",
               file=sys.stderr, flush=True)

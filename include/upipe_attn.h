@@ -63,6 +63,13 @@
  *    with events, so work after the call on `stream` sees every result.
  *    Calls on one device must not run concurrently from several host
  *    threads.
+ *  - HIP graph capture: with pipelining and profiling off (the defaults)
+ *    every entry point enqueues kernel launches on `stream` only (no
+ *    allocation, memset, event or synchronization), so a caller may
+ *    capture a forward and backward into a graph and replay it; a replay
+ *    reads whatever the captured input buffers hold at that time and gives
+ *    the eager call's bits.  The pipelined and profiled schedules use the
+ *    library's own stream and events and are not meant for capture.
  *  - Outputs are fully overwritten (never accumulated into).
  *
  * Precision

@@ -46,6 +46,8 @@
  *    the first launch (target values are device data and are not checked
  *    there, see above), on any error nothing is launched; outputs are fully
  *    overwritten; status codes are the UPIPE_* codes of upipe_attn.h.
+ *  - Every call enqueues kernel launches on `stream` only, so it may be
+ *    captured into a HIP graph and replayed (as in upipe_attn.h).
  *  - Supported: 1 <= L <= 2^24, hidden and vocab multiples of 128 (pad the
  *    vocabulary; padded rows of W take part in the softmax), hidden * vocab
  *    < 2^33, tile_rows >= 1 (a tile larger than L is L).

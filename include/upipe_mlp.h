@@ -34,6 +34,8 @@
  *    checks run on the host before the first launch, on any error nothing
  *    is launched; outputs are fully overwritten; status codes are the
  *    UPIPE_* codes of upipe_attn.h.
+ *  - Every call enqueues kernel launches on `stream` only, so it may be
+ *    captured into a HIP graph and replayed (as in upipe_attn.h).
  *  - Supported: 1 <= L <= 2^24, hidden and ffn multiples of 128 with
  *    hidden * ffn < 2^33, tile_rows >= 1 (a tile larger than L is L).
  *  - Precision: bf16 operands with fp32 accumulation; h, u, a, da, dh, du
