@@ -13,6 +13,7 @@
 //    four 32-key blocks x two 32-query halves of every tile) and walks every
 //    q head of that KV group in the chunk and every 64-query tile at or
 //    below the diagonal, accumulating dK/dV of the group in fp32 registers;
+//    each wave holds its 32 K and V rows in registers for the whole walk;
 //    the two halves' partial sums meet in LDS once, at the end.  Scores are
 //    computed S = Q K^T so each lane owns ONE key: the S/dP accumulators
 //    feed dV^T = dO^T P and dK^T = Q^T dS as MFMA B operands straight from
@@ -100,25 +101,28 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
     dma16_untracked(vp + off, lds_addr(Vs + n * 512));
   }
 
-  // per-lane element offsets, fixed for the whole loop
-  //  row-per-lane operands: Q/dO rows 32*qh + l32, chunk 2ks + g; the K/V
-  //  rows 32*kwave + l32 sit a uniform distance dko further (same swizzle)
-  int offq[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) offq[ks] = tile_off(32 * qh + l32, 2 * ks + g);
+  // per-lane element offsets.  Each is held for k step / column block 0
+  // only: the swizzle XORs chunk c of a row with swz(row) < 16, so the
+  // other steps' offsets are that one XOR a constant, rebuilt per step with
+  // one v_xor each; holding all of them would take 14 more registers, which
+  // the K rows need (below).
+  //  row-per-lane operands: Q/dO rows 32*qh + l32, chunk 2ks + g: ks is
+  //  chunk bits 1-3, element-offset bits 4-6, so offset(ks) = offq0 ^ (ks << 4);
+  //  the K/V rows 32*kwave + l32 sit a uniform distance dko further (same
+  //  swizzle)
+  const int offq0 = tile_off(32 * qh + l32, g);
   const int dko_init = (kwave - qh) * 32 * 128;
   //  transposed operands dO^T / Q^T (see tile_read_t): column block db,
-  //  rows 32*qh + 4g + (lane%16)/4 and +8; 16h more rows are an immediate
-  int offt[4][2];
+  //  rows 32*qh + 4g + (lane%16)/4 and +8; db is chunk bits 2-3, element-
+  //  offset bits 5-6, so offset(db) = offt0 ^ (db << 5); 16h more rows are
+  //  an immediate
+  int offt0[2];
   {
     const int sl = lane & 15, grp2 = (lane >> 4) & 1;
     const int r0 = 32 * qh + 4 * g + (sl >> 2);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int col = db * 32 + 16 * grp2 + 4 * (sl & 3);
-      offt[db][0] = tile_off(r0, col >> 3) + (col & 7);
-      offt[db][1] = tile_off(r0 + 8, col >> 3) + (col & 7);
-    }
+    const int col = 16 * grp2 + 4 * (sl & 3);
+    offt0[0] = tile_off(r0, col >> 3) + (col & 7);
+    offt0[1] = tile_off(r0 + 8, col >> 3) + (col & 7);
   }
   //  per-row scalars of the lane's queries 32*qh + 8*r4 + 4g + i
   const int offl = 32 * qh + 4 * g;
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
   }
 
   f32x16 acc_dk[4], acc_dv[4];
-  u32x4 vreg[8];
+  u32x4 vreg[8], kreg[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     acc_dk[i] = f32x16{};
@@ -179,7 +183,10 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
     // units; the dP accumulator starts from the tile's -D rows, so dS below
     // is one multiply per element.  (Starting S from the -LSE rows as well
     // saves the add below but delays the first MFMA behind four more reads:
-    // measured 1.2% slower.)
+    // measured 1.2% slower.)  The empty asm keeps the compiler from hoisting
+    // the eight XORed offsets out of the loop into registers.
+    int oq = offq0;
+    asm volatile("" : "+v"(oq));
     f32x16 sv = f32x16{}, dp;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -187,24 +194,18 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dp[r4 * 4 + i] = e4[i];
     }
-    // K addresses are rebuilt every step (8 adds) rather than held in 8
-    // more registers
-    uint32_t kb = lds_addr(Ks) + 2 * dko_init;
-    asm volatile("" : "+s"(kb));
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const uint32_t ka = kb + 2 * offq[ks];
-      sv = mfma32(*reinterpret_cast<const u32x4*>(Qt + offq[ks]), lds_load16(ka, 0), sv);
-      dp = mfma32(*reinterpret_cast<const u32x4*>(Ot + offq[ks]), vreg[ks], dp);
+      sv = mfma32(*reinterpret_cast<const u32x4*>(Qt + (oq ^ (ks << 4))), kreg[ks], sv);
+      dp = mfma32(*reinterpret_cast<const u32x4*>(Ot + (oq ^ (ks << 4))), vreg[ks], dp);
     }
-    // the -D rows and two k steps (six reads) ahead, then three per two
-    // MFMAs: measured 0.9% faster than LLVM's generic LDS/MFMA interleave
-    // here, which in turn was 1% faster than the compiler's default order
-    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+    // the -D rows and two k steps (four reads) ahead, then two per two
+    // MFMAs (three or four steps ahead no longer fit the registers)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if (need_mask) {  // key after the query, or a padding query row
@@ -234,17 +235,19 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
     // the dV/dK MFMAs issue at raised wave priority (the other wave of the
     // SIMD then gets the VALU slots for its P/dS work)
     __builtin_amdgcn_s_setprio(1);
+    int ot0 = offt0[0], ot1 = offt0[1];
+    asm volatile("" : "+v"(ot0), "+v"(ot1));
     // dV^T += dO^T P, dK^T += Q^T dS over this wave's 32 queries; B slot t
     // of step h is query 32*qh + 16*h + 8*(t/4) + 4*g + t%4
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const u32x2 o_lo = lds_read_tr16(Ot + offt[db][0] + h * 2048);
-        const u32x2 o_hi = lds_read_tr16(Ot + offt[db][1] + h * 2048);
+        const u32x2 o_lo = lds_read_tr16(Ot + (ot0 ^ (db << 5)) + h * 2048);
+        const u32x2 o_hi = lds_read_tr16(Ot + (ot1 ^ (db << 5)) + h * 2048);
         acc_dv[db] = mfma32(u32x4{o_lo[0], o_lo[1], o_hi[0], o_hi[1]}, pP[h], acc_dv[db]);
-        const u32x2 q_lo = lds_read_tr16(Qt + offt[db][0] + h * 2048);
-        const u32x2 q_hi = lds_read_tr16(Qt + offt[db][1] + h * 2048);
+        const u32x2 q_lo = lds_read_tr16(Qt + (ot0 ^ (db << 5)) + h * 2048);
+        const u32x2 q_hi = lds_read_tr16(Qt + (ot1 ^ (db << 5)) + h * 2048);
         acc_dk[db] = mfma32(u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}, pS[h], acc_dk[db]);
       }
     // transpose reads kept eight (four MFMAs) ahead, then two per MFMA:
@@ -263,11 +266,16 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
   if (nsteps > 0) load_next(Q0, O0, L0, E0);
   lds_dma_wait();
   __syncthreads();
-  // the wave's 32 V rows as the B operand of dP = dO V^T, held in registers
-  // for the whole loop (32 VGPRs; one of K/V fits in the budget, and V
-  // measured 2.5% faster than K; S still reads K from LDS)
+  // the wave's 32 K and 32 V rows, the B operands of S = Q K^T and
+  // dP = dO V^T, held in registers for the whole loop (64 VGPRs): each step
+  // then reads only Q, dO and their transposes from LDS (32 of 40 KB per
+  // wave with K read from LDS: measured 1.6-1.8% faster per launch)
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) vreg[ks] = lds_load16(lds_addr(Ks) + 2 * (dko_init + offq[ks]), BNK * 128 * 2);
+  for (int ks = 0; ks < 8; ++ks) {
+    const uint32_t a = lds_addr(Ks) + 2 * (dko_init + (offq0 ^ (ks << 4)));
+    kreg[ks] = lds_load16(a, 0);
+    vreg[ks] = lds_load16(a, BNK * 128 * 2);
+  }
   int qt = qs_hi - 1, hj = j0;  // step being computed: tile qt, head hj
   auto advance = [&]() {
     if (++hj == j1) {
