@@ -58,33 +58,35 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
   }
   const float nlse2 = a.lse2[(int64_t)head * a.Lp + my_q];  // -LSE, base 2
   const float ndval = a.dvec[(int64_t)head * a.Lp + my_q];  // -D
-  // the lane's -D in all 16 registers: the starting value of each dP^T
-  // chain (the first MFMA reads it as its C operand), so dP - D costs no
-  // vector instruction per element
-  f32x16 nd16;
+  // the lane's -D and -LSE in all 16 registers: the starting values of each
+  // dP^T and S^T chain (the first MFMA reads them as its C operand), so
+  // dP - D and S - LSE cost no vector instruction per element
+  f32x16 nd16, nl16;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) nd16[r] = ndval;
+  for (int r = 0; r < 16; ++r) {
+    nd16[r] = ndval;
+    nl16[r] = nlse2;
+  }
 
   const int kv_end = (q0 + QBM < L) ? q0 + QBM : L;
   const int n_kt = (kv_end + QBN - 1) / QBN;
 
   // per-lane element offsets, fixed for the whole loop
   //  K/V rows (A operands of S^T and dP^T): row kb*32 + l32, chunk 2ks + g
-  int koff[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) koff[ks] = tile_off(l32, 2 * ks + g);
+  // (held for step 0 only: the swizzle XORs a row's chunk index with a
+  // per-row constant, so step ks sits at koff0 ^ (ks << 4) and column block
+  // db of the transpose reads at offt0 ^ (db << 5), one v_xor per read;
+  // the registers go to the -LSE tuple)
+  const int koff0 = tile_off(l32, g);
   //  K^T (A operand of dQ^T, see tile_read_t): column block db, rows
   //  4g + (lane%16)/4 and +8; 16 st more rows are an immediate
-  int offt[4][2];
+  int offt0[2];
   {
     const int sl = lane & 15, grp2 = (lane >> 4) & 1;
     const int rr = 4 * g + (sl >> 2);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int col = db * 32 + 16 * grp2 + 4 * (sl & 3);
-      offt[db][0] = tile_off(rr, col >> 3) + (col & 7);
-      offt[db][1] = tile_off(rr + 8, col >> 3) + (col & 7);
-    }
+    const int col = 16 * grp2 + 4 * (sl & 3);
+    offt0[0] = tile_off(rr, col >> 3) + (col & 7);
+    offt0[1] = tile_off(rr + 8, col >> 3) + (col & 7);
   }
   //  tile copies: wave w moves rows 16w .. 16w+15 of the K and V tiles
   uint32_t tdma[4];
@@ -114,15 +116,17 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
     f32x16 sv[2], dp[2];
     // the S/dP MFMAs issue at raised wave priority, the rest at the default
     // (measured: the dQ MFMAs at raised priority too is slower)
+    int ko = koff0;
+    asm volatile("" : "+v"(ko));  // keeps the XORed offsets out of registers
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      sv[kb] = f32x16{};
+      sv[kb] = nl16;
       dp[kb] = nd16;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        sv[kb] = mfma32(*reinterpret_cast<const u32x4*>(Kt + koff[ks] + kb * 4096), qreg[ks], sv[kb]);
-        dp[kb] = mfma32(*reinterpret_cast<const u32x4*>(Vt + koff[ks] + kb * 4096), doreg[ks], dp[kb]);
+        sv[kb] = mfma32(*reinterpret_cast<const u32x4*>(Kt + (ko ^ (ks << 4)) + kb * 4096), qreg[ks], sv[kb]);
+        dp[kb] = mfma32(*reinterpret_cast<const u32x4*>(Vt + (ko ^ (ks << 4)) + kb * 4096), doreg[ks], dp[kb]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sv[kb][r] + nlse2);
+        const float p = __builtin_amdgcn_exp2f(sv[kb][r]);
         ds[r] = p * dp[kb][r];
       }
 #pragma unroll
@@ -148,13 +152,15 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(BwdArgs a) {
         for (int t = 0; t < 4; ++t)
           pS[kb * 2 + h][t] = pack_bf16x2(ds[8 * h + 2 * t], ds[8 * h + 2 * t + 1]);
     }
+    int ot0 = offt0[0], ot1 = offt0[1];
+    asm volatile("" : "+v"(ot0), "+v"(ot1));
     // dQ^T += K^T dS^T; B slot t of step st is key 16*st + 8*(t/4) + 4*g + t%4
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const u32x2 lo = lds_read_tr16(Kt + offt[db][0] + st * 2048);
-        const u32x2 hi = lds_read_tr16(Kt + offt[db][1] + st * 2048);
+        const u32x2 lo = lds_read_tr16(Kt + (ot0 ^ (db << 5)) + st * 2048);
+        const u32x2 hi = lds_read_tr16(Kt + (ot1 ^ (db << 5)) + st * 2048);
         acc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pS[st], acc[db]);
       }
     // K^T transpose reads kept six (three MFMAs) ahead, then two per MFMA

@@ -29,9 +29,10 @@
 //    sum is taken from the same fp16 P by v_dot2_f32_f16, so numerator and
 //    denominator see identical probabilities;
 //  * the softmax runs in base 2: q arrives multiplied by log2(e)/sqrt(d), so
-//    the score MFMAs produce base-2 exponents directly; the running maximum
-//    is raised lazily (only when a score exceeds it by more than 2^8), which
-//    removes the per-tile rescale of O;
+//    the score MFMAs produce base-2 exponents directly, and their chains
+//    start from -(running maximum), so they produce the exponents of P
+//    themselves; the running maximum is raised lazily (only when a score
+//    exceeds it by more than 2^8), which removes the per-tile rescale of O;
 //  * the two LDS buffers are distinct arrays and the key loop is unrolled
 //    by two, so every LDS address is a per-lane base plus an immediate and
 //    the compiler can see that reads of one buffer never alias the copy in
@@ -95,15 +96,14 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   const int kv_end = (q0 + BM < L) ? q0 + BM : L;
   const int n_kt = (kv_end + BN - 1) / BN;
 
-  // per-lane element offsets, fixed for the whole loop
+  // per-lane element offsets, held for step 0 only: the swizzles XOR a
+  // row's chunk index with a per-row constant, so step ks (st) sits at the
+  // step-0 offset XOR ks << 4 (st << 4), one v_xor per read, which leaves
+  // the registers for the -m_run tuple below
   //  K reads (A operand of S^T): row kb*32 + l32, chunk 2ks + g
-  int koff[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) koff[ks] = tile_off(l32, 2 * ks + g);
+  const int koff0 = tile_off(l32, g);
   //  V^T reads (A operand of O^T): row db*32 + l32, chunk 2st + g
-  int voff[4];
-#pragma unroll
-  for (int st = 0; st < 4; ++st) voff[st] = l32 * 64 + (((2 * st + g) ^ ((l32 >> 1) & 7)) << 3);
+  const int voff0 = l32 * 64 + ((g ^ ((l32 >> 1) & 7)) << 3);
   //  K tile copy: wave w moves rows 16w .. 16w+15, four 1 KB pieces
   uint32_t kdma[4];
 #pragma unroll
@@ -131,17 +131,30 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   // (base 2) when it is given (padding rows: 0, their O is not stored)
   float m_run = -__builtin_inff();
   if (FROM_LSE) m_run = my_q < L ? a.lse_in[(int64_t)(a.q_head0 + head) * L + my_q] * kLog2e : 0.f;
+  // -m_run in all 16 registers: the starting value (C operand) of the next
+  // tile's score chains, so the scores come out as s - m_run and the
+  // exponentials need no subtraction; sref is the maximum the held scores
+  // are relative to (tile 0 is computed from 0 before m_run exists)
+  f32x16 nm16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nm16[r] = -m_run;
+  float sref = FROM_LSE ? m_run : 0.f;
   float l_run = 0.f;
   const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 
   // S^T of one key tile: element (key kb*32 + acc_row(r,g), query my_q)
-  auto scores = [&](const uint16_t* Kc, f32x16* s) {
+  auto scores = [&](const uint16_t* Kc, f32x16* s, bool from_zero) {
+    int ko = koff0;
+    asm volatile("" : "+v"(ko));  // keeps the XORed offsets out of registers
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+      if (from_zero)
+        s[kb] = f32x16{};
+      else
+        s[kb] = nm16;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        s[kb] = mfma32(*reinterpret_cast<const u32x4*>(Kc + koff[ks] + kb * 4096), qreg[ks], s[kb]);
+        s[kb] = mfma32(*reinterpret_cast<const u32x4*>(Kc + (ko ^ (ks << 4)) + kb * 4096), qreg[ks], s[kb]);
     }
   };
 
@@ -174,17 +187,26 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
       for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[0][r]), sc[0][r + 1]);
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[1][r]), sc[1][r + 1]);
-      mx = half_max_swap(mx);
+      mx = half_max_swap(mx) + sref;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) acc_o[db] *= alpha;
+        // the held scores move to the new reference (0 for lanes whose
+        // maximum stays), and so do the next tile's chains
+        const float d = m_new - sref;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[kb][r] -= d;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) nm16[r] = -m_new;
         m_run = m_new;
+        sref = m_new;
       }
     }
-    const float mc = m_run;
     // scores of the next tile (unused past the last tile or the diagonal;
     // the buffer then holds stale but finite-or-ignored data)
     f32x16 sn[2];
@@ -193,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     // at the default: measured 2.5% faster than raising the PV MFMAs
     // instead, 6% faster than raising both
     __builtin_amdgcn_s_setprio(1);
-    scores(Knext, sn);
+    scores(Knext, sn, false);
     // LLVM's MFMA / exponential interleave strategy for this block (the
     // next tile's score MFMAs with this tile's exponentials): measured 1%
     // faster than the default schedule; the simpler variant (3) was slower
@@ -206,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       float pr[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(sc[kb][r] - mc);
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(sc[kb][r]);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -225,13 +247,15 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     l_run += ls0 + ls1;
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
+    int vo = voff0;
+    asm volatile("" : "+v"(vo));  // keeps the XORed offsets out of registers
     // O^T += V^T P^T; B slot t of step st is key 16*st + 8*(t/4) + 4*g + t%4,
     // the order in which the V^T tile stores the keys of each 16-key step
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        acc_o[db] = mfma32_f16(*reinterpret_cast<const u32x4*>(Vc + voff[st] + db * 2048), pb[st], acc_o[db]);
+        acc_o[db] = mfma32_f16(*reinterpret_cast<const u32x4*>(Vc + (vo ^ (st << 4)) + db * 2048), pb[st], acc_o[db]);
     // V^T reads kept four MFMAs ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -249,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   if (n_kt > 1) dma_k(1, K1);
   lds_dma_wait();
   __syncthreads();
-  scores(K0, sc);   // tile 0 is visible to every wave
+  scores(K0, sc, !FROM_LSE);   // tile 0 is visible to every wave
   __syncthreads();  // K0 is refilled below
   for (int kt = 0; kt < n_kt; kt += 2) {
     // K1 = tile kt+1, V0 = tile kt
