@@ -184,8 +184,8 @@ __global__ __launch_bounds__(DKDV_THREADS) void flash_bwd_dkdv_kernel(BwdArgs a)
     // is one multiply per element.  (Starting S from the -LSE rows as well
     // saves the add below but delays the first MFMA behind four more reads:
     // measured 1.2% slower, and 0.8% with K in registers.)  The empty asm
-    // keeps the compiler from hoisting
-    // the eight XORed offsets out of the loop into registers.
+    // keeps the compiler from hoisting the eight XORed offsets out of the
+    // loop into registers.
     int oq = offq0;
     asm volatile("" : "+v"(oq));
     f32x16 sv = f32x16{}, dp;
