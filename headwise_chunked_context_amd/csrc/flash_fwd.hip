@@ -96,14 +96,19 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
   const int kv_end = (q0 + BM < L) ? q0 + BM : L;
   const int n_kt = (kv_end + BN - 1) / BN;
 
-  // per-lane element offsets, held for step 0 only: the swizzles XOR a
+  // per-lane element offsets, fixed for the whole loop (the swizzles XOR a
   // row's chunk index with a per-row constant, so step ks (st) sits at the
-  // step-0 offset XOR ks << 4 (st << 4), one v_xor per read, which leaves
-  // the registers for the -m_run tuple below
+  // step-0 offset XOR ks << 4 (st << 4))
   //  K reads (A operand of S^T): row kb*32 + l32, chunk 2ks + g
   const int koff0 = tile_off(l32, g);
+  int koff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = koff0 ^ (ks << 4);
   //  V^T reads (A operand of O^T): row db*32 + l32, chunk 2st + g
   const int voff0 = l32 * 64 + ((g ^ ((l32 >> 1) & 7)) << 3);
+  int voff[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) voff[st] = voff0 ^ (st << 4);
   //  K tile copy: wave w moves rows 16w .. 16w+15, four 1 KB pieces
   uint32_t kdma[4];
 #pragma unroll
@@ -144,8 +149,6 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
 
   // S^T of one key tile: element (key kb*32 + acc_row(r,g), query my_q)
   auto scores = [&](const uint16_t* Kc, f32x16* s, bool from_zero) {
-    int ko = koff0;
-    asm volatile("" : "+v"(ko));  // keeps the XORed offsets out of registers
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (from_zero)
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
         s[kb] = nm16;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        s[kb] = mfma32(*reinterpret_cast<const u32x4*>(Kc + (ko ^ (ks << 4)) + kb * 4096), qreg[ks], s[kb]);
+        s[kb] = mfma32(*reinterpret_cast<const u32x4*>(Kc + koff[ks] + kb * 4096), qreg[ks], s[kb]);
     }
   };
 
@@ -247,15 +250,13 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     l_run += ls0 + ls1;
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
-    int vo = voff0;
-    asm volatile("" : "+v"(vo));  // keeps the XORed offsets out of registers
     // O^T += V^T P^T; B slot t of step st is key 16*st + 8*(t/4) + 4*g + t%4,
     // the order in which the V^T tile stores the keys of each 16-key step
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        acc_o[db] = mfma32_f16(*reinterpret_cast<const u32x4*>(Vc + (vo ^ (st << 4)) + db * 2048), pb[st], acc_o[db]);
+        acc_o[db] = mfma32_f16(*reinterpret_cast<const u32x4*>(Vc + voff[st] + db * 2048), pb[st], acc_o[db]);
     // V^T reads kept four MFMAs ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
