@@ -36,12 +36,12 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-file additions.  The dQ kernel's own file takes LLVM's max-ILP machine
-# scheduler: measured 2.5% faster for that kernel than the default strategy,
-# which stays for the others (the dK/dV kernel measured 3% slower with it).
-FILE_FLAGS = {
-    "flash_bwd_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-}
+# Per-file additions (none at present).  The dQ kernel's file once took
+# LLVM's max-ILP machine scheduler (-mllvm -amdgpu-sched-strategy=max-ilp),
+# 2.5% faster for the kernel of that time; with its score chains started
+# from the -LSE tuple the default strategy is 0.5% faster, and the dK/dV
+# kernel always measured 3% slower with max-ILP.
+FILE_FLAGS: dict[str, list[str]] = {}
 
 
 def _hipcc() -> str:
