@@ -391,3 +391,16 @@ def test_choose_chunk_takes_the_largest_chunk_that_fits(shape):
     with pytest.raises(B.UpipeError) as e:
         hc_amd.choose_chunk(L, D, nq, nkv, 1 << 40, 7)
     assert e.value.status == B.UPIPE_EINVAL
+
+
+def test_autograd_wrappers_import_without_gpu():
+    """The autograd module imports on a host without a GPU and exposes one
+    torch.autograd.Function per forward / backward pair."""
+    import torch
+
+    from headwise_chunked_context_amd import autograd as ag
+
+    for f in (ag._Attention, ag._SwiGluMlp, ag._CrossEntropy):
+        assert issubclass(f, torch.autograd.Function)
+    for fn in (ag.attention, ag.swiglu_mlp, ag.cross_entropy):
+        assert callable(fn)
