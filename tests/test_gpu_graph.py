@@ -189,3 +189,36 @@ def test_loss_step_replays_from_graph(fused):
     label = f"loss L={w.L} tile={tile} {'fused' if fused else 'separate'}"
     ref = _replay_and_compare(torch, fill, step, out, g, label)
     check(ref, draws[0], tile, f"graph {label}")
+
+
+def test_static_forward_replays_from_graph():
+    """The allocation-free forward (static scratch, caller-allocated outputs)
+    recorded into a graph: the capture allocates nothing, and each replay on
+    fresh inputs equals the workspace forward's bits."""
+    import headwise_chunked_context_amd as lib
+
+    torch = _torch()
+    L, hidden, nq, nkv, hc = 1000, 512, 8, 2, 2
+    w = synthetic.WORKLOADS[1].with_(L=L, hidden=hidden, n_q=nq, n_kv=nkv, head_chunk=hc)
+    draws = [synthetic.make_inputs(w, with_grad=False, seed_base=_seed(r)) for r in range(REPLAYS)]
+    names = ("x", "w_qkv", "w_o")
+    x, wq, wo = (to_dev(draws[0][k]) for k in names)
+    out = (torch.empty(L, hidden, dtype=torch.bfloat16, device="cuda:0"),
+           torch.empty(L, nq * 128, dtype=torch.bfloat16, device="cuda:0"),
+           torch.empty(nq, L, dtype=torch.float32, device="cuda:0"))
+    lib.attn_fwd_static(x, wq, wo, nq, nkv, hc, w.theta, out=out)   # scratch looked up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.attn_fwd_static(x, wq, wo, nq, nkv, hc, w.theta, out=out)
+
+    def fill(rep):
+        for t, k in zip((x, wq, wo), names):
+            t.copy_(to_dev(draws[rep][k]))
+
+    def eager():
+        y, o, lse = lib.attn_fwd(x, wq, wo, nq, nkv, hc, w.theta)
+        return dict(y=y, o=o, lse=lse)
+
+    _replay_and_compare(torch, fill, eager, dict(y=out[0], o=out[1], lse=out[2]), g,
+                        f"static forward L={L} hidden={hidden} hc={hc}")
