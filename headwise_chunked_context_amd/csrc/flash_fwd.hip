@@ -222,6 +222,8 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FwdArgs a) {
     // LLVM's MFMA / exponential interleave strategy for this block (the
     // next tile's score MFMAs with this tile's exponentials): measured 1%
     // faster than the default schedule; the simpler variant (3) was slower
+    // (with the scores starting from -m_run: default 1.8%, variant 1 0.6%
+    // slower)
     __builtin_amdgcn_iglp_opt(2);
     // P in fp16, packed in pairs as the B operand; the row sum is taken
     // from each fp16 pair before it goes into the operand vector
