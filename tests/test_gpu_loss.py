@@ -317,3 +317,28 @@ def test_fused_llama3_vocabulary_and_debug_fill():
         assert torch.equal(g[k].view(torch.int32), dbg[k].view(torch.int32)), k
     for k in ("dh", "dw"):
         assert torch.equal(g[k].view(torch.int16), dbg[k].view(torch.int16)), k
+
+
+def _random_loss_shapes(n, seed=20261204):
+    """Seeded loss shapes: hidden and vocabulary multiples of 128, ragged L,
+    tiles from one row to longer than the sequence, the separate passes and
+    the fused call alternating, upstream gradients other than 1."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        L = int(rng.integers(1, 1500))
+        D = 128 * int(rng.integers(1, 6))
+        V = 128 * int(rng.integers(1, 13))
+        tile = int(rng.choice([1, 7, 64, 256, 300, 777, 4096]))
+        dloss = float(rng.choice([1.0, 0.5, 3.0]))
+        out.append((L, D, V, tile, dloss, bool(i % 2), int(rng.integers(0, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("L,D,V,tile,dloss,fused,seed", _random_loss_shapes(8))
+def test_random_loss_shapes_match_oracle(L, D, V, tile, dloss, fused, seed):
+    w = synthetic.LOSS_WORKLOADS[21].with_(L=L, hidden=D, vocab=V, tile_rows=tile)
+    inp = synthetic.make_loss_inputs(w, seed_base=seed)
+    g = run_fused(inp, tile, dloss) if fused else run_gpu(inp, tile, dloss)
+    check(g, inp, tile, f"random loss L={L} D={D} V={V} tile={tile} dloss={dloss} "
+          f"{'fused' if fused else 'separate'} seed={seed}", dloss=dloss)

@@ -172,3 +172,24 @@ def test_debug_nan_fill_changes_nothing():
     for k in ("dwgu", "dwd"):
         assert np.isfinite(from_dev_bf16(dbg[k])).all()
         assert rel_l2(from_dev_bf16(dbg[k]), from_dev_bf16(ref[k])) <= 1e-3, k
+
+
+def _random_mlp_shapes(n, seed=20261203):
+    """Seeded MLP shapes: hidden and intermediate multiples of 128, ragged L,
+    tiles from one row to longer than the sequence."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        L = int(rng.integers(1, 1500))
+        D = 128 * int(rng.integers(1, 6))
+        F = 128 * int(rng.integers(1, 9))
+        tile = int(rng.choice([1, 7, 64, 256, 300, 777, 4096]))
+        out.append((L, D, F, tile, int(rng.integers(0, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("L,D,F,tile,seed", _random_mlp_shapes(8))
+def test_random_mlp_shapes_match_oracle(L, D, F, tile, seed):
+    w = synthetic.MLP_WORKLOADS[11].with_(L=L, hidden=D, ffn=F, tile_rows=tile)
+    inp = synthetic.make_mlp_inputs(w, seed_base=seed)
+    check(run_gpu(inp, tile), inp, tile, f"random mlp L={L} D={D} F={F} tile={tile} seed={seed}")
